@@ -1,0 +1,152 @@
+"""Seeded synthetic inputs for exact attention forward and KV-cache decode.
+
+This module is shared by the CPU oracle and the GPU path. It holds no part of
+the attention arithmetic: it only draws random numbers, rounds them to the
+16-bit storage formats, and converts stored bit patterns back to float64.
+
+Workloads follow the shapes the pages use. The SDPA page ("Flash Attention 2 ...
+PyTorch native", devhandbook.co.kr, Example 1 and Example 5) draws
+``torch.randn`` tensors in (B, H, L, D) layout, including grouped K/V with fewer
+heads; the KV-cache page ("Advanced techniques for enhancing LLM throughput",
+cabseo.com, section "Memory requirements") gives the per-sequence cache that
+decode reads.
+
+Seeding: every (tensor, batch, head) slab has its own NumPy substream
+``default_rng([seed, tensor_id, b, head])`` with tensor_id Q=0, K=1, V=2, so a
+slab can be regenerated alone (long-context row samples, per-head oracles).
+Values are float32 ``standard_normal`` draws in row-major (row, dim) order,
+rounded to nearest-even into bf16 or fp16.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+__all__ = [
+    "BF16", "FP16", "Q_ID", "K_ID", "V_ID",
+    "round_to_bits", "bits_to_f64", "slab", "prefill_inputs",
+    "decode_lengths", "decode_inputs", "sample_rows", "CONFIGS",
+]
+
+BF16 = "bf16"
+FP16 = "fp16"
+Q_ID, K_ID, V_ID = 0, 1, 2
+BF16_NAN_BITS = 0x7FC0
+FP16_NAN_BITS = 0x7E00
+
+# The five workloads: shapes, dtype, mask. Seed of config k is k.
+CONFIGS = {
+    "c1_tiny_mha": dict(seed=1, B=1, Hq=8, Hkv=8, N=128, d=64, dtype=BF16, causal=(False,)),
+    "c2_mid_mha": dict(seed=2, B=2, Hq=8, Hkv=8, N=4096, d=64, dtype=FP16, causal=(False, True)),
+    "c3_llama3_8b_gqa": dict(seed=3, B=1, Hq=32, Hkv=8, N=8192, d=128, dtype=BF16, causal=(True,)),
+    "c4_long_context": dict(seed=4, B=1, Hq=32, Hkv=8, N=131072, d=128, dtype=BF16, causal=(True,),
+                            sample_rows=256),
+    "c5_decode": dict(seed=5, B=32, Hq=32, Hkv=8, Lcap=32768, d=128, dtype=BF16,
+                      len_lo=1024, len_hi=32768),
+}
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def round_to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 values to nearest-even bf16/fp16; return uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == FP16:
+        return x.astype(np.float16).view(np.uint16)
+    if dtype != BF16:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    u = x.view(np.uint32)
+    # round-to-nearest-even on the upper 16 bits; inputs here are finite
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    out = ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = BF16_NAN_BITS
+    return out
+
+
+def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact widening of stored bf16/fp16 bit patterns to float64."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    if dtype == FP16:
+        return bits.view(np.float16).astype(np.float64)
+    if dtype != BF16:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def slab(seed: int, tensor_id: int, b: int, head: int, n: int, d: int, dtype: str) -> np.ndarray:
+    """One (n, d) slab of N(0,1) values rounded to ``dtype``, as uint16 bits."""
+    rng = np.random.default_rng([seed, tensor_id, b, head])
+    return round_to_bits(rng.standard_normal(size=(n, d), dtype=np.float32), dtype)
+
+
+def _fill(out: np.ndarray, seed: int, tensor_id: int, n: int, d: int, dtype: str) -> None:
+    B, H = out.shape[0], out.shape[1]
+
+    def job(bh):
+        b, h = divmod(bh, H)
+        out[b, h, :n] = slab(seed, tensor_id, b, h, n, d, dtype)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(job, range(B * H)))
+
+
+def prefill_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str,
+                   Nk: int | None = None) -> dict:
+    """Q [B,Hq,N,d], K/V [B,Hkv,Nk,d] as uint16 bit arrays (contiguous)."""
+    Nk = N if Nk is None else Nk
+    q = np.empty((B, Hq, N, d), np.uint16)
+    k = np.empty((B, Hkv, Nk, d), np.uint16)
+    v = np.empty((B, Hkv, Nk, d), np.uint16)
+    _fill(q, seed, Q_ID, N, d, dtype)
+    _fill(k, seed, K_ID, Nk, d, dtype)
+    _fill(v, seed, V_ID, Nk, d, dtype)
+    return dict(q=q, k=k, v=v, dtype=dtype)
+
+
+def decode_lengths(seed: int, B: int, lo: int, hi: int) -> np.ndarray:
+    """Per-sequence cache lengths, uniform on [lo, hi] inclusive, int32."""
+    rng = np.random.default_rng([seed, 3])
+    return rng.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+
+
+def decode_inputs(seed: int, B: int, Hq: int, Hkv: int, Lcap: int, d: int, dtype: str,
+                  lengths: np.ndarray) -> dict:
+    """q [B,Hq,d]; k/v caches [B,Hkv,Lcap,d]; rows >= lengths[b] hold NaN bits."""
+    lengths = np.asarray(lengths, np.int32)
+    nan_bits = BF16_NAN_BITS if dtype == BF16 else FP16_NAN_BITS
+    q = np.empty((B, Hq, d), np.uint16)
+    for b in range(B):
+        for h in range(Hq):
+            q[b, h] = slab(seed, Q_ID, b, h, 1, d, dtype)[0]
+    kc = np.empty((B, Hkv, Lcap, d), np.uint16)
+    vc = np.empty((B, Hkv, Lcap, d), np.uint16)
+
+    def job(args):
+        cache, tid, b, g = args
+        L = int(min(max(lengths[b], 0), Lcap))
+        cache[b, g, :L] = slab(seed, tid, b, g, L, d, dtype)
+        cache[b, g, L:] = nan_bits
+
+    work = [(c, t, b, g) for (c, t) in ((kc, K_ID), (vc, V_ID)) for b in range(B) for g in range(Hkv)]
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(job, work))
+    return dict(q=q, k_cache=kc, v_cache=vc, seqlens=lengths, dtype=dtype)
+
+
+def sample_rows(seed: int, head: int, N: int, count: int = 256) -> np.ndarray:
+    """Sorted distinct query rows for a per-head spot check: 0, N-1 and count-2 others."""
+    if N <= count:
+        return np.arange(N, dtype=np.int64)
+    rng = np.random.default_rng([seed, 4, head])
+    mid = rng.choice(np.arange(1, N - 1), size=count - 2, replace=False)
+    return np.sort(np.concatenate([[0, N - 1], mid]).astype(np.int64))

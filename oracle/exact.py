@@ -1,0 +1,145 @@
+"""Plain float64 attention: the definition, written out (TEST INFRASTRUCTURE).
+
+Source: "Flash Attention: Revolutionizing Transformer Efficiency" (unite.ai),
+the standard-attention listing that opens the page: scores are Q times K
+transposed divided by the square root of the head width, a softmax over the
+key axis, then a product with V. The same page, section "The math of Flash
+Attention", gives the softmax decomposition used here (subtract the row maximum
+before exponentiating); that only guards against overflow and leaves the exact
+value unchanged. FlashAttention computes exactly this result, not an
+approximation (same page, section "Impact of Flash Attention", point 3).
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+  * scale: the caller passes it; the library receives a float32, so the oracle
+    uses the float64 value of that float32 (``as_fp32_scale``).
+  * causal mask (SDPA page, Example 3, ``is_causal``): bottom-right aligned,
+    key j is visible to query i iff j <= i + (Nk - Nq).
+  * grouped-query heads (SDPA page, Example 5): q-head h reads kv-head
+    h // (Hq // Hkv), i.e. K/V repeated contiguously along the head axis.
+  * LSE: natural log of the sum of exp over the visible, scaled scores.
+  * a row with no visible key: O = 0 and LSE = -inf.
+  * decode (throughput page, "Memory requirements"): the new token of
+    sequence b attends, unmasked, to cache rows [0, L_b).
+
+This module is test infrastructure. Only tests, the smoke check and the CPU
+baseline of the benchmark may use it.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def as_fp32_scale(scale: float) -> float:
+    """The float64 value of the float32 the C boundary receives."""
+    return float(np.float32(scale))
+
+
+def scores(q: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    """S = scale * Q K^T for one head: q [Nq,d], k [Nk,d] -> [Nq,Nk] float64."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    return as_fp32_scale(scale) * (q @ k.T)
+
+
+def visibility(Nq: int, Nk: int, causal: bool) -> np.ndarray:
+    """Boolean [Nq,Nk]: which keys each query may attend to."""
+    if not causal:
+        return np.ones((Nq, Nk), dtype=bool)
+    i = np.arange(Nq)[:, None]
+    j = np.arange(Nk)[None, :]
+    return j <= i + (Nk - Nq)
+
+
+def softmax_rows(S: np.ndarray, vis: np.ndarray):
+    """Row softmax over visible entries. Returns (P, m, l).
+
+    m is the row maximum over visible scores, l = sum exp(S - m) over visible
+    entries, P = exp(S - m) / l (0 where hidden). Rows with nothing visible get
+    m = -inf, l = 0, P = 0.
+    """
+    Sm = np.where(vis, S, -np.inf)
+    m = Sm.max(axis=1) if Sm.shape[1] else np.full(Sm.shape[0], -np.inf)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    e = np.where(vis, np.exp(Sm - m_safe[:, None]), 0.0)
+    l = e.sum(axis=1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        P = np.where(l[:, None] > 0, e / np.where(l > 0, l, 1.0)[:, None], 0.0)
+    return P, m, l
+
+
+def attention_head(q, k, v, scale, causal=False):
+    """One head: q [Nq,d], k/v [Nk,d] -> (O [Nq,d], LSE [Nq]) in float64."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    S = scores(q, k, scale)
+    P, m, l = softmax_rows(S, visibility(q.shape[0], k.shape[0], causal))
+    O = P @ v
+    with np.errstate(divide="ignore"):
+        lse = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    return O, lse
+
+
+def _kv_head(h: int, Hq: int, Hkv: int) -> int:
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return h // (Hq // Hkv)
+
+
+def attention(q, k, v, scale, causal=False):
+    """q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] (float64) -> O [B,Hq,Nq,d], LSE [B,Hq,Nq]."""
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    O = np.zeros((B, Hq, Nq, v.shape[3]), np.float64)
+    L = np.zeros((B, Hq, Nq), np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            O[b, h], L[b, h] = attention_head(q[b, h], k[b, g], v[b, g], scale, causal)
+    return O, L
+
+
+def attention_rows(q_rows, rows, k, v, scale, causal, Nq):
+    """Selected query rows of one head.
+
+    q_rows [R,d] are the query vectors of rows ``rows`` (absolute indices in a
+    query sequence of length Nq); k/v [Nk,d]. Exactly the rows of
+    ``attention_head`` over the full sequence, without the other rows.
+    """
+    q_rows = np.asarray(q_rows, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    rows = np.asarray(rows, np.int64)
+    Nk = k.shape[0]
+    S = scores(q_rows, k, scale)
+    if causal:
+        vis = np.arange(Nk)[None, :] <= rows[:, None] + (Nk - Nq)
+    else:
+        vis = np.ones_like(S, dtype=bool)
+    P, m, l = softmax_rows(S, vis)
+    with np.errstate(divide="ignore"):
+        lse = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
+    return P @ v, lse
+
+
+def decode(q, k_cache, v_cache, seqlens, scale):
+    """One new token per sequence against its cache.
+
+    q [B,Hq,d]; caches [B,Hkv,Lcap,d]; seqlens [B] -> O [B,Hq,d], LSE [B,Hq].
+    Rows at or beyond L_b are never read (they may hold NaN).
+    """
+    B, Hq, d = q.shape
+    Hkv, Lcap = k_cache.shape[1], k_cache.shape[2]
+    O = np.zeros((B, Hq, v_cache.shape[3]), np.float64)
+    L = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = int(min(max(int(seqlens[b]), 0), Lcap))
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            o, lse = attention_head(np.asarray(q[b, h], np.float64)[None, :],
+                                    np.asarray(k_cache[b, g, :n], np.float64),
+                                    np.asarray(v_cache[b, g, :n], np.float64), scale, False)
+            O[b, h], L[b, h] = o[0], lse[0]
+    return O, L

@@ -1,0 +1,319 @@
+"""Checks that pin the float64 oracle to facts that do not come from itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with a
+closed form, an invariant, a pure-Python brute force, a library routine, or a
+hand-worked fixture. ``test_oracle_pins.py`` runs them on the real oracle;
+``test_oracle_mutations.py`` plants plausible mistakes in the oracle and checks
+that at least one pin then fails.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+from oracle import exact as oa
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TOL = 1e-12
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _expr(s: str) -> float:
+    return float(eval(s, {"__builtins__": {}}, {"exp": math.exp, "log": math.log}))
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- brute force
+def brute_force(q, k, v, scale, causal):
+    """Pure-Python scalar loops, no NumPy arithmetic: q [B,Hq,Nq,d] nested lists."""
+    B, Hq, Nq = len(q), len(q[0]), len(q[0][0])
+    Hkv, Nk = len(k[0]), len(k[0][0])
+    sigma = float(np.float32(scale))
+    grp = Hq // Hkv
+    O, L = [], []
+    for b in range(B):
+        Ob, Lb = [], []
+        for h in range(Hq):
+            g = h // grp
+            Oh, Lh = [], []
+            for i in range(Nq):
+                s = {}
+                for j in range(Nk):
+                    if causal and j > i + (Nk - Nq):
+                        continue
+                    acc = 0.0
+                    for t in range(len(q[b][h][i])):
+                        acc += q[b][h][i][t] * k[b][g][j][t]
+                    s[j] = sigma * acc
+                if not s:
+                    Oh.append([0.0] * len(v[b][g][0]))
+                    Lh.append(-math.inf)
+                    continue
+                m = max(s.values())
+                e = {j: math.exp(x - m) for j, x in s.items()}
+                l = sum(e.values())
+                Oh.append([sum(e[j] * v[b][g][j][c] for j in e) / l for c in range(len(v[b][g][0]))])
+                Lh.append(m + math.log(l))
+            Ob.append(Oh)
+            Lb.append(Lh)
+        O.append(Ob)
+        L.append(Lb)
+    return np.array(O), np.array(L)
+
+
+def pin_brute_force():
+    r = _rng(11)
+    cases = [(1, 1, 1, 1, 1, 1), (1, 2, 2, 2, 2, 2), (1, 2, 2, 3, 3, 4), (2, 4, 1, 5, 5, 8),
+             (1, 4, 2, 17, 17, 4), (1, 4, 1, 3, 7, 2), (1, 2, 2, 5, 9, 8)]
+    for (B, Hq, Hkv, Nq, Nk, d) in cases:
+        q = r.standard_normal((B, Hq, Nq, d)) * 1.5
+        k = r.standard_normal((B, Hkv, Nk, d))
+        v = r.standard_normal((B, Hkv, Nk, d))
+        scale = 1.0 / math.sqrt(d)
+        for causal in (False, True):
+            if causal and Nq > Nk:
+                continue
+            O, L = oracle.attention(q, k, v, scale, causal)
+            Ob, Lb = brute_force(q.tolist(), k.tolist(), v.tolist(), scale, causal)
+            assert np.abs(O - Ob).max() <= TOL, (B, Hq, Hkv, Nq, Nk, d, causal)
+            assert np.abs(L - Lb).max() <= TOL, (B, Hq, Hkv, Nq, Nk, d, causal)
+
+
+# ---------------------------------------------------------------- closed forms
+def pin_single_key_and_causal_row0():
+    r = _rng(12)
+    for d in (1, 4, 64):
+        q = r.standard_normal((1, d))
+        k = r.standard_normal((1, d))
+        v = r.standard_normal((1, d))
+        O, L = oracle.attention_head(q, k, v, 0.3)
+        assert np.array_equal(O[0], v[0])
+        s00 = float(np.float32(0.3)) * float(np.dot(q[0], k[0]))
+        assert abs(L[0] - s00) <= TOL * max(1.0, abs(s00))
+    q = r.standard_normal((9, 8))
+    k = r.standard_normal((9, 8))
+    v = r.standard_normal((9, 8))
+    O, L = oracle.attention_head(q, k, v, 0.25, causal=True)
+    assert np.array_equal(O[0], v[0])
+    assert abs(L[0] - float(np.float32(0.25)) * float(np.dot(q[0], k[0]))) <= TOL
+
+
+def pin_two_keys():
+    r = _rng(13)
+    for d in (1, 3, 16):
+        q = r.standard_normal((3, d))
+        k = r.standard_normal((2, d))
+        v = r.standard_normal((2, d))
+        sc = 0.7
+        O, L = oracle.attention_head(q, k, v, sc)
+        s = float(np.float32(sc)) * (q @ k.T)
+        exp_o = v[1][None, :] + (v[0] - v[1])[None, :] / (1.0 + np.exp(s[:, 1] - s[:, 0]))[:, None]
+        assert np.abs(O - exp_o).max() <= TOL
+        assert np.abs(L - np.logaddexp(s[:, 0], s[:, 1])).max() <= TOL
+
+
+def pin_golden_fixtures():
+    g = load_golden("two_keys_d2.json")
+    O, L = oracle.attention_head(np.array(g["q"]), np.array(g["k"]), np.array(g["v"]), g["scale"], g["causal"])
+    want_o = np.array([[_expr(x) for x in row] for row in g["expected_o"]])
+    want_l = np.array([_expr(x) for x in g["expected_lse"]])
+    assert np.abs(O - want_o).max() <= TOL and np.abs(L - want_l).max() <= TOL
+    u = load_golden("uniform_q0.json")
+    for causal, ko, kl in ((False, "noncausal_o", "noncausal_lse"), (True, "causal_o", "causal_lse")):
+        O, L = oracle.attention_head(np.array(u["q"]), np.array(u["k"]), np.array(u["v"]), u["scale"], causal)
+        want_o = np.array([[_expr(x) for x in row] for row in u[ko]])
+        want_l = np.array([_expr(x) for x in u[kl]])
+        assert np.abs(O - want_o).max() <= TOL and np.abs(L - want_l).max() <= TOL
+
+
+def pin_zero_query():
+    r = _rng(14)
+    N, d = 33, 8
+    k = r.standard_normal((N, d))
+    v = r.standard_normal((N, d))
+    q = np.zeros((N, d))
+    O, L = oracle.attention_head(q, k, v, 0.5)
+    assert np.abs(O - v.mean(axis=0)[None, :]).max() <= TOL
+    assert np.abs(L - math.log(N)).max() <= TOL
+    O, L = oracle.attention_head(q, k, v, 0.5, causal=True)
+    prefix = np.cumsum(v, axis=0) / np.arange(1, N + 1)[:, None]
+    assert np.abs(O - prefix).max() <= TOL
+    assert np.abs(L - np.log(np.arange(1, N + 1))).max() <= TOL
+
+
+# ---------------------------------------------------------------- invariants
+def pin_rows_sum_to_one():
+    r = _rng(15)
+    S = r.standard_normal((20, 30)) * 4
+    for causal in (False, True):
+        vis = oa.visibility(20, 30, causal)
+        P, m, l = oa.softmax_rows(S, vis)
+        assert np.abs(P.sum(axis=1) - 1.0).max() <= TOL
+        assert np.all(P[~vis] == 0)
+        assert np.all(P[vis] > 0)
+    q = r.standard_normal((10, 4))
+    k = r.standard_normal((12, 4))
+    O, _ = oracle.attention_head(q, k, np.ones((12, 3)), 1.0, causal=True)
+    assert np.abs(O - 1.0).max() <= TOL
+
+
+def pin_merge_identity():
+    r = _rng(16)
+    N, d = 300, 8
+    q = r.standard_normal((N, d))
+    k = r.standard_normal((N, d))
+    v = r.standard_normal((N, d))
+    for causal in (False, True):
+        O, L = oracle.attention_head(q, k, v, 0.35, causal)
+        for bq, bk in ((1, 1), (7, 7), (64, 64), (256, 256), (N, N), (64, 7), (13, 256)):
+            Ob, Lb = oracle.blockwise_attention_head(q, k, v, 0.35, causal, bq, bk)
+            assert np.abs(Ob - O).max() <= TOL and np.abs(Lb - L).max() <= TOL, (bq, bk, causal)
+    # random split of the keys into chunks, each normalised on its own, then merged
+    O, L = oracle.attention_head(q, k, v, 0.35)
+    cuts = np.sort(r.choice(np.arange(1, N), size=5, replace=False))
+    bounds = [0, *cuts.tolist(), N]
+    parts = [oracle.attention_head(q, k[a:b], v[a:b], 0.35) for a, b in zip(bounds[:-1], bounds[1:])]
+    Om, Lm = oracle.merge_partials([p[0] for p in parts], [p[1] for p in parts])
+    assert np.abs(Om - O).max() <= TOL and np.abs(Lm - L).max() <= TOL
+    # an empty part (no keys) contributes nothing
+    empty_o, empty_l = np.zeros_like(O), np.full(N, -np.inf)
+    Om2, Lm2 = oracle.merge_partials([p[0] for p in parts] + [empty_o], [p[1] for p in parts] + [empty_l])
+    assert np.abs(Om2 - O).max() <= TOL and np.abs(Lm2 - L).max() <= TOL
+
+
+def pin_shift_invariance():
+    r = _rng(17)
+    q = r.standard_normal((6, 5))
+    k = r.standard_normal((9, 5))
+    v = r.standard_normal((9, 5))
+    u = r.standard_normal(5)
+    sc = 0.6
+    O, L = oracle.attention_head(q, k, v, sc)
+    O2, L2 = oracle.attention_head(q, k + u[None, :], v, sc)
+    assert np.abs(O2 - O).max() <= 1e-11
+    assert np.abs(L2 - (L + float(np.float32(sc)) * (q @ u))).max() <= 1e-11
+
+
+def pin_permutation():
+    r = _rng(18)
+    q = r.standard_normal((7, 4))
+    k = r.standard_normal((11, 4))
+    v = r.standard_normal((11, 4))
+    O, L = oracle.attention_head(q, k, v, 0.9)
+    pk = r.permutation(11)
+    O2, L2 = oracle.attention_head(q, k[pk], v[pk], 0.9)
+    assert np.abs(O2 - O).max() <= TOL and np.abs(L2 - L).max() <= TOL
+    pq = r.permutation(7)
+    O3, L3 = oracle.attention_head(q[pq], k, v, 0.9)
+    assert np.abs(O3 - O[pq]).max() <= TOL and np.abs(L3 - L[pq]).max() <= TOL
+
+
+def pin_convex_hull():
+    r = _rng(19)
+    q = r.standard_normal((12, 4)) * 3
+    k = r.standard_normal((12, 4))
+    v = r.standard_normal((12, 6))
+    for causal in (False, True):
+        O, _ = oracle.attention_head(q, k, v, 1.0, causal)
+        vis = oa.visibility(12, 12, causal)
+        for i in range(12):
+            lo = v[vis[i]].min(axis=0)
+            hi = v[vis[i]].max(axis=0)
+            assert np.all(O[i] >= lo - TOL) and np.all(O[i] <= hi + TOL)
+
+
+def pin_causal_is_prefix():
+    r = _rng(20)
+    Nq, Nk, d = 6, 10, 4
+    q = r.standard_normal((Nq, d))
+    k = r.standard_normal((Nk, d))
+    v = r.standard_normal((Nk, d))
+    O, L = oracle.attention_head(q, k, v, 0.5, causal=True)
+    for i in range(Nq):
+        n = i + (Nk - Nq) + 1
+        Oi, Li = oracle.attention_head(q[i:i + 1], k[:n], v[:n], 0.5)
+        assert np.abs(Oi[0] - O[i]).max() <= TOL and abs(Li[0] - L[i]) <= TOL
+
+
+def pin_gqa_is_repeated_mha():
+    r = _rng(21)
+    B, Hq, Hkv, N, d = 2, 8, 2, 9, 4
+    q = r.standard_normal((B, Hq, N, d))
+    k = r.standard_normal((B, Hkv, N, d))
+    v = r.standard_normal((B, Hkv, N, d))
+    for causal in (False, True):
+        O, L = oracle.attention(q, k, v, 0.5, causal)
+        kr = np.repeat(k, Hq // Hkv, axis=1)
+        vr = np.repeat(v, Hq // Hkv, axis=1)
+        for b in range(B):
+            for h in range(Hq):
+                Oh, Lh = oracle.attention_head(q[b, h], kr[b, h], vr[b, h], 0.5, causal)
+                assert np.abs(Oh - O[b, h]).max() <= TOL and np.abs(Lh - L[b, h]).max() <= TOL
+
+
+def pin_decode_is_single_query():
+    r = _rng(22)
+    B, Hq, Hkv, Lcap, d = 3, 4, 2, 20, 8
+    lens = np.array([1, 13, 20])
+    q = r.standard_normal((B, Hq, d))
+    kc = r.standard_normal((B, Hkv, Lcap, d))
+    vc = r.standard_normal((B, Hkv, Lcap, d))
+    for b in range(B):
+        kc[b, :, lens[b]:] = np.nan
+        vc[b, :, lens[b]:] = np.nan
+    O, L = oracle.decode(q, kc, vc, lens, 0.4)
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            Oh, Lh = brute_force([[[q[b, h].tolist()]]], [[kc[b, g, :lens[b]].tolist()]],
+                                 [[vc[b, g, :lens[b]].tolist()]], 0.4, False)
+            assert np.abs(Oh[0, 0, 0] - O[b, h]).max() <= TOL and abs(Lh[0, 0, 0] - L[b, h]) <= TOL
+    # an empty sequence yields zeros and -inf
+    O0, L0 = oracle.decode(q[:1], kc[:1], vc[:1], np.array([0]), 0.4)
+    assert np.all(O0 == 0) and np.all(np.isneginf(L0))
+
+
+def pin_lse_library():
+    r = _rng(23)
+    q = r.standard_normal((8, 4)) * 2
+    k = r.standard_normal((8, 4)) * 2
+    v = r.standard_normal((8, 4))
+    for causal in (False, True):
+        _, L = oracle.attention_head(q, k, v, 0.8, causal)
+        s = float(np.float32(0.8)) * (q @ k.T)
+        vis = oa.visibility(8, 8, causal)
+        for i in range(8):
+            assert abs(L[i] - np.logaddexp.reduce(s[i][vis[i]])) <= TOL
+
+
+def pin_sampled_rows_match_full():
+    r = _rng(24)
+    N, d = 40, 8
+    q = r.standard_normal((N, d))
+    k = r.standard_normal((N, d))
+    v = r.standard_normal((N, d))
+    rows = np.array([0, 3, 17, 39])
+    for causal in (False, True):
+        O, L = oracle.attention_head(q, k, v, 0.5, causal)
+        Os, Ls = oracle.attention_rows(q[rows], rows, k, v, 0.5, causal, N)
+        assert np.abs(Os - O[rows]).max() <= TOL and np.abs(Ls - L[rows]).max() <= TOL
+
+
+ALL_PINS = [
+    pin_brute_force, pin_single_key_and_causal_row0, pin_two_keys, pin_golden_fixtures,
+    pin_zero_query, pin_rows_sum_to_one, pin_merge_identity, pin_shift_invariance,
+    pin_permutation, pin_convex_hull, pin_causal_is_prefix, pin_gqa_is_repeated_mha,
+    pin_decode_is_single_query, pin_lse_library, pin_sampled_rows_match_full,
+]
