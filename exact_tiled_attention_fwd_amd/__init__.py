@@ -1,0 +1,214 @@
+"""Exact attention forward (FlashAttention-2 style) on MI355X / gfx950.
+
+A thin ctypes binding over the C ABI of ``include/fa.h`` (``libfa.so``, built
+by ``exact_tiled_attention_fwd_amd.build``). Every step of the computation
+runs in the HIP kernels of that library; this module only marshals arguments.
+PyTorch supplies device memory and the current stream.
+
+Raw entry points, same names and argument order as the C header:
+    fa_fwd, fa_decode, fa_decode_workspace_bytes, fa_status_string,
+    fa_last_error, fa_abi_version
+Tensor-level helpers:
+    attention(q, k, v, causal=False, scale=None) -> (o, lse)
+    decode(q, k_cache, v_cache, seqlens, scale=None, num_splits=0) -> (o, lse)
+
+There is no fallback: if the library is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # loads the HIP runtime that libfa.so then binds to
+
+__all__ = [
+    "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
+    "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FAError", "lib_path", "load_library",
+    "fa_fwd", "fa_decode", "fa_decode_workspace_bytes", "fa_status_string",
+    "fa_last_error", "fa_abi_version", "attention", "decode", "dtype_code",
+]
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_DTYPE_BF16, FA_DTYPE_FP16 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libfa.so")
+
+
+class FAError(RuntimeError):
+    """A non-OK status from the library (status code in ``.status``)."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class FAInvalidArgument(FAError, ValueError):
+    pass
+
+
+class FAUnsupported(FAError, NotImplementedError):
+    pass
+
+
+def load_library():
+    """Load libfa.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library not found at {path}; build it with "
+            "`python -m exact_tiled_attention_fwd_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
+    lib.fa_decode.restype = i
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_abi_version.argtypes = []
+    lib.fa_abi_version.restype = i
+    _LIB = lib
+    return lib
+
+
+def _raise_for(status: int):
+    if status == FA_OK:
+        return
+    lib = load_library()
+    msg = f"{lib.fa_status_string(status).decode()}: {lib.fa_last_error().decode()}"
+    if status == FA_ERR_INVALID_ARG:
+        raise FAInvalidArgument(status, msg)
+    if status == FA_ERR_UNSUPPORTED:
+        raise FAUnsupported(status, msg)
+    raise FAError(status, msg)
+
+
+# ------------------------------------------------------------------ raw C ABI
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, stream) -> int:
+    """Call the C ``fa_fwd`` with integer device addresses; returns the status."""
+    return load_library().fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, stream)
+
+
+def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, workspace_bytes,
+              B, Hq, Hkv, Lcap, d, scale, num_splits, dtype, stream) -> int:
+    """Call the C ``fa_decode`` with integer device addresses; returns the status."""
+    return load_library().fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, workspace_bytes,
+                                    B, Hq, Hkv, Lcap, d, scale, num_splits, dtype, stream)
+
+
+def fa_decode_workspace_bytes(B, Hq, Hkv, Lcap, d, num_splits) -> int:
+    return load_library().fa_decode_workspace_bytes(B, Hq, Hkv, Lcap, d, num_splits)
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(status).decode()
+
+
+def fa_last_error() -> str:
+    return load_library().fa_last_error().decode()
+
+
+def fa_abi_version() -> int:
+    return load_library().fa_abi_version()
+
+
+# ------------------------------------------------------------------ torch helpers
+def dtype_code(dt) -> int:
+    if dt == torch.bfloat16:
+        return FA_DTYPE_BF16
+    if dt == torch.float16:
+        return FA_DTYPE_FP16
+    raise FAUnsupported(FA_ERR_UNSUPPORTED, f"unsupported dtype {dt}; use bfloat16 or float16")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _check_tensor(name, t, ndim, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must be a torch.Tensor")
+    if t.dim() != ndim:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} is on {t.device}, expected {device}")
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """O, LSE for q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] (bf16/fp16, contiguous, same GPU)."""
+    _check_tensor("q", q, 4)
+    dev = q.device
+    _check_tensor("k", k, 4, dev)
+    _check_tensor("v", v, 4, dev)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "q, k and v must share a dtype")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (Bk, dk) != (B, d) or tuple(v.shape) != tuple(k.shape):
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        st = fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                    float(scale), int(bool(causal)), dtype_code(q.dtype), _stream(dev))
+    _raise_for(st)
+    return out, lse
+
+
+def decode(q, k_cache, v_cache, seqlens, scale: float | None = None, num_splits: int = 0,
+           workspace=None, out=None, lse=None):
+    """One new token per sequence: q [B,Hq,d], caches [B,Hkv,Lcap,d], seqlens int32 [B]."""
+    _check_tensor("q", q, 3)
+    dev = q.device
+    _check_tensor("k_cache", k_cache, 4, dev)
+    _check_tensor("v_cache", v_cache, 4, dev)
+    _check_tensor("seqlens", seqlens, 1, dev)
+    if seqlens.dtype != torch.int32:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "seqlens must be int32")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "q and the caches must share a dtype")
+    B, Hq, d = q.shape
+    Bk, Hkv, Lcap, dk = k_cache.shape
+    if (Bk, dk) != (B, d) or tuple(v_cache.shape) != tuple(k_cache.shape) or seqlens.shape[0] != B:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "shape mismatch between q, caches and seqlens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_decode_workspace_bytes(B, Hq, Hkv, Lcap, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        st = fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(out), _ptr(lse),
+                       _ptr(workspace), workspace.numel() * workspace.element_size(),
+                       B, Hq, Hkv, Lcap, d, float(scale), int(num_splits), dtype_code(q.dtype), _stream(dev))
+    _raise_for(st)
+    return out, lse

@@ -1,0 +1,51 @@
+// fa_launch.h - internal interface between the C ABI (fa_api.cpp) and the
+// kernel translation units. Not installed; callers use include/fa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+  int dtype;
+};
+
+// Decode key split: chunk keys per workgroup, n_split chunks cover Lcap rows.
+struct DecodePlan {
+  int chunk;
+  int n_split;
+  size_t ws_lse_offset;  // bytes from workspace start to the LSE partials
+  size_t ws_bytes;       // total workspace bytes
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* seqlens;
+  void* o;
+  float* lse;
+  void* workspace;
+  size_t ws_lse_offset;
+  int B, Hq, Hkv, Lcap, d;
+  float scale;
+  int chunk, n_split;
+  int dtype;
+};
+
+constexpr int kDecodeTileRows = 128;
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace fa

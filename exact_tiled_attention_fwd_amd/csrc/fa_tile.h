@@ -1,0 +1,201 @@
+// fa_tile.h - gfx950 device building blocks shared by the prefill and decode
+// kernels: HBM->register->LDS tile movement, matrix-core (MFMA) operand
+// fetches, and the online-softmax step.
+//
+// The arithmetic follows "Flash Attention: Revolutionizing Transformer
+// Efficiency" (unite.ai), sections "The math of Flash Attention" (subtract the
+// running maximum; merge partial softmaxes by rescaling with exp(m_old-m_new))
+// and "Implementation details" (running max M and running sum L per query
+// row). The output accumulator is kept unnormalised and divided by the row
+// sum once at the end (FlashAttention-2's deferred normalisation).
+//
+// Orientation. Both products run on the 32x32x16 MFMA with the contraction
+// index contiguous in each lane:
+//   S^T[key][query] = K[key][:] . Q[query][:]          (A = K tile, B = Q^T)
+//   O^T[d][query]  += V^T[d][key] . P^T[key][query]    (A = V^T tile, B = P^T)
+// The S^T accumulator holds, in lane l, query column l%32 and 16 keys, so the
+// per-query max and sum are lane-local up to one exchange with lane l^32, and
+// the accumulator registers are already the B operand of the second product
+// once rounded to 16 bits. V is transposed while it is written to LDS, with the
+// keys of each 16-key group stored in the order the accumulator holds them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+enum { DT_BF16 = 0, DT_FP16 = 1 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Geometry of one K/V tile of ROWS keys and head width D, as laid out in LDS.
+//   K   : row-major [ROWS][D] 16-bit, 16-byte chunks XOR-swizzled per row so
+//         that the 32 rows an MFMA operand fetch touches hit distinct banks.
+//   V^T : [D][ROWS] 16-bit plus 16 bytes of padding per row; keys permuted
+//         within each group of 16 (see vt_pos).
+template <int D, int ROWS>
+struct Tile {
+  static_assert(D == 64 || D == 128, "head width");
+  static_assert(ROWS % 64 == 0, "tile rows");
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per K row
+  static constexpr int KB = ROWS / 32;               // 32-key blocks
+  static constexpr int KS = D / 16;                  // MFMA k-steps over d
+  static constexpr int MT = D / 32;                  // 32-row blocks of O^T
+  static constexpr int K_BYTES = ROWS * D * 2;
+  static constexpr int VT_STRIDE = ROWS * 2 + 16;
+  static constexpr int VT_BYTES = D * VT_STRIDE;
+  static constexpr int STAGE_BYTES = K_BYTES + VT_BYTES;
+  static constexpr int UNITS = (ROWS / 4) * CPR;     // (4 keys x 16 bytes) units
+  static constexpr int U = UNITS / 256;              // units per thread (256 threads)
+  static_assert(UNITS % 256 == 0, "tile/threads");
+
+  __device__ static inline int swz(int row) { return (row / (16 / CPR)) % CPR; }
+};
+
+// ------------------------------------------------------------------ HBM -> regs
+// Thread t moves U units; unit = 4 consecutive rows x one 16-byte chunk. Within
+// a wave the 64 lanes cover 16 row-quads x 4 chunks, which keeps the global
+// loads in 64-byte runs per row and the transposed LDS writes conflict-free.
+template <int D, int ROWS>
+struct TileRegs {
+  u32x4 k[Tile<D, ROWS>::U][4];
+  u32x4 v[Tile<D, ROWS>::U][4];
+};
+
+template <int D, int ROWS>
+__device__ inline void unit_coords(int p, int& kq, int& c) {
+  constexpr int CG = Tile<D, ROWS>::CPR / 4;  // chunk groups per row
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wu = w + 4 * p;
+  kq = 16 * (wu / CG) + (lane & 15);
+  c = 4 * (wu % CG) + (lane >> 4);
+}
+
+// Load rows [0, nvalid) of a tile whose first row is at kbase/vbase (row
+// stride D elements). Rows at or beyond nvalid are zero-filled and never read.
+template <int D, int ROWS>
+__device__ inline void load_tile(const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase,
+                                 int nvalid, TileRegs<D, ROWS>& r) {
+#pragma unroll
+  for (int p = 0; p < Tile<D, ROWS>::U; ++p) {
+    int kq, c;
+    unit_coords<D, ROWS>(p, kq, c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * kq + i;
+      if (row < nvalid) {
+        const size_t off = (size_t)row * D + (size_t)c * 8;
+        r.k[p][i] = *reinterpret_cast<const u32x4*>(kbase + off);
+        r.v[p][i] = *reinterpret_cast<const u32x4*>(vbase + off);
+      } else {
+        r.k[p][i] = u32x4{0u, 0u, 0u, 0u};
+        r.v[p][i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+}
+
+// Position (in elements) of key kk (0..15) inside its 16-key group of V^T: the
+// accumulator of S^T holds, in lane half h and element e of an 8-element
+// operand, key 8*(e/4) + 4*h + e%4; V^T stores that key at position 8*h + e,
+// so one 16-byte read per lane yields the matching A operand.
+__device__ inline int vt_quad_pos(int quad) {  // quad = kk/4 in 0..3
+  return (quad == 1) ? 2 : (quad == 2) ? 1 : quad;
+}
+
+// ------------------------------------------------------------------ regs -> LDS
+template <int D, int ROWS>
+__device__ inline void store_tile(char* __restrict__ stage, const TileRegs<D, ROWS>& r) {
+  using T = Tile<D, ROWS>;
+  char* kl = stage;
+  char* vl = stage + T::K_BYTES;
+#pragma unroll
+  for (int p = 0; p < T::U; ++p) {
+    int kq, c;
+    unit_coords<D, ROWS>(p, kq, c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * kq + i;
+      *reinterpret_cast<u32x4*>(kl + row * (D * 2) + ((c ^ T::swz(row)) * 16)) = r.k[p][i];
+    }
+    // V^T: 8 head-dim rows, each gets the 4 keys of this row-quad (8 bytes).
+    const int grp = kq >> 2;
+    const int pos = 16 * grp + 4 * vt_quad_pos(kq & 3);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t a0 = r.v[p][0][t], a1 = r.v[p][1][t], a2 = r.v[p][2][t], a3 = r.v[p][3][t];
+      // element 2t (low halves) and 2t+1 (high halves) of the 4 rows
+      const u32x2 even = {__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
+      const u32x2 odd = {__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
+      const int d0 = 8 * c + 2 * t;
+      *reinterpret_cast<u32x2*>(vl + d0 * T::VT_STRIDE + pos * 2) = even;
+      *reinterpret_cast<u32x2*>(vl + (d0 + 1) * T::VT_STRIDE + pos * 2) = odd;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ operands
+// A operand of S^T = K Q^T: key row 32*kb + lane%32, d = 16*ks + 8*(lane/32) .. +7
+template <int D, int ROWS>
+__device__ inline u32x4 k_operand(const char* __restrict__ stage, int kb, int ks, int lane) {
+  using T = Tile<D, ROWS>;
+  const int row = 32 * kb + (lane & 31);
+  const int chunk = 2 * ks + (lane >> 5);
+  return *reinterpret_cast<const u32x4*>(stage + row * (D * 2) + ((chunk ^ T::swz(row)) * 16));
+}
+
+// A operand of O^T += V^T P^T: d row 32*mt + lane%32, 16-key group G, half lane/32
+template <int D, int ROWS>
+__device__ inline u32x4 vt_operand(const char* __restrict__ stage, int mt, int G, int lane) {
+  using T = Tile<D, ROWS>;
+  const int d = 32 * mt + (lane & 31);
+  return *reinterpret_cast<const u32x4*>(stage + T::K_BYTES + d * T::VT_STRIDE + G * 32 + (lane >> 5) * 16);
+}
+
+// ------------------------------------------------------------------ MFMA
+template <int DT>
+__device__ inline f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (DT == DT_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// Round two fp32 to the 16-bit type (nearest-even), packed low/high.
+template <int DT>
+__device__ inline uint32_t pack2(float lo, float hi) {
+  const f32x2 f = {lo, hi};
+  if constexpr (DT == DT_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max / sum of x over lanes l and l^32. v_permlane32_swap(x, x) returns, in
+// every lane, the pair {x[l & 31], x[(l & 31) + 32]}.
+__device__ inline float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Key offset (within a 32-key block) of accumulator register r in lane half h.
+__device__ inline int acc_key(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+}  // namespace fa

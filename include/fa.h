@@ -1,0 +1,139 @@
+/*
+ * fa.h - exact attention forward (FlashAttention-2 style) and split-KV decode
+ * for AMD Instinct MI355X (gfx950). C ABI: plain pointers and sizes only.
+ *
+ * What is computed (the plain definition, "Flash Attention: Revolutionizing
+ * Transformer Efficiency", unite.ai, standard-attention listing):
+ *
+ *     O = softmax(scale * Q K^T [+ causal mask]) V,   LSE = log sum exp(...)
+ *
+ * per (batch, q-head, query row), without ever forming the score matrix: K/V
+ * tiles stream through on-chip memory and the row maximum and row sum are
+ * carried block to block with the softmax-merge identity of the same page
+ * (section "The math of Flash Attention"). The result equals the plain
+ * definition up to floating-point rounding (same page, "Impact", point 3).
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, contiguous, row-major, on the device that is
+ *     current for the calling thread, 16-byte aligned.
+ *   - Element type of q, k, v, o, caches: bf16 or fp16 (argument `dtype`);
+ *     arithmetic: fp32 accumulation on matrix cores; O is rounded to
+ *     nearest-even into `dtype`; LSE is fp32 (natural log).
+ *   - Grouped-query attention (SDPA page, devhandbook.co.kr, Example 5): q-head
+ *     h reads kv-head h / (Hq / Hkv); Hq must be a multiple of Hkv. Hkv = 1 is
+ *     multi-query attention.
+ *   - `stream` is a hipStream_t passed as void* (NULL = legacy default stream).
+ *     Work is only enqueued; the call never synchronises, allocates or frees.
+ *     Results are valid once the stream has completed.
+ *   - Inputs are read-only; outputs must not alias inputs.
+ *   - Ownership: the caller allocates and frees every buffer, including the
+ *     decode workspace. The library keeps only per-device properties.
+ *   - Errors: every argument is validated before anything is enqueued; on
+ *     failure nothing is written and the call returns a status. The text of
+ *     the most recent failure on the calling thread is fa_last_error().
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,  /* null/misaligned pointer, bad size, bad scale, ... */
+  FA_ERR_UNSUPPORTED = 2,  /* head dim, dtype or device not supported */
+  FA_ERR_HIP = 3           /* the HIP runtime reported an error */
+} fa_status;
+
+typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP16 = 1 } fa_dtype;
+
+/*
+ * fa_fwd - prefill attention forward.
+ *
+ * Source of the operation: "Flash Attention: Revolutionizing Transformer
+ * Efficiency" (unite.ai): standard-attention listing (definition), sections
+ * "Flash Attention algorithm" and "Implementation details" (tiled loop over
+ * query blocks and key/value blocks with running max and sum). Causal masking
+ * as `is_causal` in the SDPA page (devhandbook.co.kr), Example 3.
+ *
+ *   q   [B, Hq,  Nq, d]  input, dtype
+ *   k   [B, Hkv, Nk, d]  input, dtype
+ *   v   [B, Hkv, Nk, d]  input, dtype
+ *   o   [B, Hq,  Nq, d]  output, dtype
+ *   lse [B, Hq,  Nq]     output, fp32, natural-log sum of exp of the visible
+ *                        scaled scores; may be NULL (then not written)
+ *   d      head width: 64 or 128 (else FA_ERR_UNSUPPORTED)
+ *   scale  multiplies Q K^T; finite and > 0 (typically 1/sqrt(d))
+ *   causal 0 or 1. With causal, key j is visible to query i iff
+ *          j <= i + (Nk - Nq) (bottom-right alignment); requires Nq <= Nk.
+ *   dtype  FA_DTYPE_BF16 or FA_DTYPE_FP16
+ *
+ * Sizes must be positive; B*Hq*Nq*d and B*Hkv*Nk*d must fit in int64.
+ * Returns FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                 int dtype, void* stream);
+
+/*
+ * fa_decode_workspace_bytes - bytes of device workspace fa_decode needs for
+ * these sizes and this `num_splits` (0 = the library's choice). Returns 0 if
+ * the sizes are invalid. The workspace holds per-split partial outputs and
+ * their LSE (the merge identity in LSE form).
+ */
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Lcap, int d, int num_splits);
+
+/*
+ * fa_decode - one new query token per sequence against its KV cache, split
+ * along the keys, then merged.
+ *
+ * Source: "Advanced techniques for enhancing LLM throughput" (cabseo.com),
+ * sections "Memory requirements" (each new token attends to the cached K/V of
+ * every earlier token) and "Autoregressive and memory-bound operations"
+ * (decode is a matrix-vector product bound by memory traffic). The split
+ * results are merged with the softmax-merge identity of the unite.ai page
+ * ("The math of Flash Attention"), in LSE form:
+ *     LSE = log sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) O_s.
+ *
+ *   q        [B, Hq, d]          input, dtype
+ *   k_cache  [B, Hkv, Lcap, d]   input, dtype; rows >= seqlens[b] are never read
+ *   v_cache  [B, Hkv, Lcap, d]   input, dtype; rows >= seqlens[b] are never read
+ *   seqlens  [B] int32, device memory; values are clamped to [0, Lcap]. A
+ *            sequence of length 0 yields O = 0 and LSE = -inf.
+ *   o        [B, Hq, d]          output, dtype
+ *   lse      [B, Hq] fp32 output, may be NULL
+ *   workspace, workspace_bytes: device scratch of at least
+ *            fa_decode_workspace_bytes(...) bytes, 256-byte aligned, owned by
+ *            the caller; contents on entry are ignored.
+ *   d        64 or 128; Hq / Hkv must be <= 32
+ *   scale    finite and > 0
+ *   num_splits  number of key chunks per sequence for a cache of Lcap rows,
+ *            0 = chosen by the library; the result does not depend on it
+ *            beyond rounding.
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARG (including a too-small workspace),
+ * FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
+                    void* o, float* lse, void* workspace, size_t workspace_bytes,
+                    int B, int Hq, int Hkv, int Lcap, int d, float scale, int num_splits,
+                    int dtype, void* stream);
+
+/* Static text for a status code. */
+const char* fa_status_string(int status);
+
+/* Detail of the most recent failure on the calling thread ("" if none). */
+const char* fa_last_error(void);
+
+/* Library ABI version (incremented on incompatible changes). */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

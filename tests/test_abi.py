@@ -1,0 +1,131 @@
+"""The C-ABI library loads, exports what include/fa.h declares, and rejects bad
+arguments before touching a device (these calls run without a GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_fwd_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_built_and_loads():
+    assert os.path.exists(fa.lib_path()), "run exact_tiled_attention_fwd_amd.build first"
+    lib = fa.load_library()
+    assert lib.fa_abi_version() == 1
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"fa_fwd", "fa_decode", "fa_decode_workspace_bytes", "fa_status_string", "fa_last_error"} <= set(names)
+    raw = ctypes.CDLL(fa.lib_path())
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared in fa.h but not exported"
+
+
+def test_status_strings():
+    assert fa.fa_status_string(0) == "FA_OK"
+    assert fa.fa_status_string(1) == "FA_ERR_INVALID_ARG"
+    assert fa.fa_status_string(2) == "FA_ERR_UNSUPPORTED"
+    assert fa.fa_status_string(3) == "FA_ERR_HIP"
+    assert fa.fa_status_string(99) == "FA_UNKNOWN_STATUS"
+
+
+def fwd(**kw):
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, lse=None,
+             B=1, Hq=8, Hkv=8, Nq=128, Nk=128, d=64, scale=0.125, causal=0, dtype=0, stream=None)
+    a.update(kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
+                     a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=FAKE + 8), fa.FA_ERR_INVALID_ARG),            # misaligned
+    (dict(lse=FAKE + 0x400002), fa.FA_ERR_INVALID_ARG),   # misaligned lse
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=1, Nq=129, Nk=128), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-0.1), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=2), fa.FA_ERR_UNSUPPORTED),
+    (dict(o=FAKE + 0x1000), fa.FA_ERR_INVALID_ARG),       # o overlaps q
+    (dict(lse=FAKE + 0x200100), fa.FA_ERR_INVALID_ARG),   # lse overlaps v
+])
+def test_fwd_rejects_before_launch(kw, status):
+    st = fwd(**kw)
+    assert st == status, (st, fa.fa_last_error())
+    assert fa.fa_last_error() != ""
+
+
+def dec(**kw):
+    a = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, seqlens=FAKE + 0x3000000, o=FAKE + 0x3100000,
+             lse=None, ws=FAKE + 0x4000000, ws_bytes=1 << 30, B=2, Hq=8, Hkv=2, Lcap=1024, d=128,
+             scale=0.088, num_splits=0, dtype=0, stream=None)
+    a.update(kw)
+    return fa.fa_decode(a["q"], a["k"], a["v"], a["seqlens"], a["o"], a["lse"], a["ws"], a["ws_bytes"],
+                        a["B"], a["Hq"], a["Hkv"], a["Lcap"], a["d"], a["scale"], a["num_splits"],
+                        a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(seqlens=None), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=None), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=FAKE + 0x4000010), fa.FA_ERR_INVALID_ARG),   # workspace not 256-aligned
+    (dict(seqlens=FAKE + 0x3000002), fa.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), fa.FA_ERR_INVALID_ARG),           # too small
+    (dict(Lcap=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID_ARG),
+    (dict(num_splits=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(Hq=64, Hkv=1), fa.FA_ERR_UNSUPPORTED),          # > 32 q-heads per kv-head
+    (dict(o=FAKE + 0x10), fa.FA_ERR_INVALID_ARG),         # o overlaps q
+])
+def test_decode_rejects_before_launch(kw, status):
+    st = dec(**kw)
+    assert st == status, (st, fa.fa_last_error())
+
+
+def test_decode_workspace_bytes():
+    # auto plan for the 32-sequence, 32K-cache shape: 512-key chunks, 64 splits
+    n = fa.fa_decode_workspace_bytes(32, 32, 8, 32768, 128, 0)
+    rows = 32 * 32 * 64
+    assert n == rows * 128 * 4 + rows * 4
+    # explicit splits: chunk rounded up to a multiple of 128 keys
+    n1 = fa.fa_decode_workspace_bytes(1, 4, 1, 1000, 64, 3)   # chunk 334 -> 384, 3 splits
+    assert n1 == (4 * 3 * 64 * 4 + 255) // 256 * 256 + 256
+    assert fa.fa_decode_workspace_bytes(1, 4, 1, 1000, 64, 1) == 4 * 64 * 4 + 256
+    assert fa.fa_decode_workspace_bytes(0, 4, 1, 1000, 64, 0) == 0
+    assert fa.fa_decode_workspace_bytes(1, 4, 1, 1000, 96, 0) == 0
+    assert fa.fa_decode_workspace_bytes(1, 4, 1, 1000, 64, -1) == 0
+
+
+def test_python_helpers_validate_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        fa.attention(torch.zeros(1, 1, 4, 64), torch.zeros(1, 1, 4, 64), torch.zeros(1, 1, 4, 64))
+    with pytest.raises(NotImplementedError):
+        fa.dtype_code(torch.float32)
