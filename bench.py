@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Benchmark: exact attention forward (prefill) and split-KV decode on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * prefill fa_fwd on the Llama-3-8B-shaped layer (B=1, Hq=32, Hkv=8,
+    N=8192, d=128, causal, bf16), the configuration the metric is quoted on;
+  * decode fa_decode (split + combine) for 32 sequences x 1 token, Hq=32,
+    Hkv=8, d=128, bf16, cache lengths uniform in [1024, 32768].
+Inputs are generated once, copied to HBM, and stay resident; the timed region
+holds only the library calls. Each call is bracketed by HIP events on the
+stream it is launched on.
+
+Prints ONE JSON line on stdout. `value` is prefill TFLOP/s counting
+4*B*Hq*Nq*Nk*d FLOPs halved for causal; `decode` carries decode GB/s counting
+the K/V rows actually read plus q, o and lse. `roofline` is the prefill
+kernel against the bf16 dense MFMA peak; `decode.roofline` the decode split
+kernel against HBM peak. `cpu_baseline` times the float64 oracle on a bounded
+sample of the same workload on the host cores.
+
+Other modes (used to take rocprofv3 counter readings):
+  --calibrate-copy   time a plain device copy of known size (counter scale)
+  --config NAME      a single configuration (c1_tiny_mha, c2_mid_mha,
+                     c2_mid_mha_causal, c3_llama3_8b_gqa, c4_long_context,
+                     c5_decode)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import attn_inputs as ai  # noqa: E402
+
+MFMA_PEAK_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_tiled_attention_fwd_amd", "csrc", f)
+                  for f in ("fa_tile.h", "fa_fwd.hip", "fa_decode.hip", "fa_launch.h", "fa_api.cpp")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ accounting
+def prefill_flops(B, Hq, Nq, Nk, d, causal):
+    f = 4.0 * B * Hq * Nq * Nk * d
+    return f / 2 if causal else f
+
+
+def prefill_bytes(B, Hq, Hkv, Nq, Nk, d, elem=2):
+    """Q, K, V read once; O and LSE written once."""
+    return elem * (2 * B * Hq * Nq * d + 2 * B * Hkv * Nk * d) + 4 * B * Hq * Nq
+
+
+def decode_bytes(lens, Hq, Hkv, d, elem=2):
+    """K/V rows actually read, plus q read, o and lse written."""
+    B = len(lens)
+    kv = sum(int(L) for L in lens) * Hkv * d * 2 * elem
+    return kv + 2 * elem * B * Hq * d + 4 * B * Hq
+
+
+def kv_cache_bytes(seq_len, layers, hidden, bytes_per_value):
+    """Per-sequence cache size: 2 (K and V) x layers x hidden x bytes per token."""
+    return seq_len * 2 * layers * hidden * bytes_per_value
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(name):
+    """HBM bytes per launch from a committed counter summary, if it matches
+    the current kernel sources; else None."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_src or not m_b or m_src.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+# ------------------------------------------------------------------ device data
+def to_dev(bits, dtype):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16 if dtype == ai.BF16 else torch.float16).cuda()
+
+
+class Prefill:
+    def __init__(self, fa, name, causal):
+        import torch
+        c = ai.CONFIGS[name]
+        self.fa, self.name, self.causal = fa, name, causal
+        self.B, self.Hq, self.Hkv, self.N, self.d, self.dtype = c["B"], c["Hq"], c["Hkv"], c["N"], c["d"], c["dtype"]
+        t0 = time.time()
+        x = ai.prefill_inputs(c["seed"], self.B, self.Hq, self.Hkv, self.N, self.d, self.dtype)
+        self.q, self.k, self.v = to_dev(x["q"], self.dtype), to_dev(x["k"], self.dtype), to_dev(x["v"], self.dtype)
+        del x
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((self.B, self.Hq, self.N), dtype=torch.float32, device="cuda")
+        self.flops = prefill_flops(self.B, self.Hq, self.N, self.N, self.d, causal)
+        self.bytes = prefill_bytes(self.B, self.Hq, self.Hkv, self.N, self.N, self.d)
+        log(f"[bench] {name} causal={causal}: inputs ready in {time.time() - t0:.1f}s")
+
+    def __call__(self):
+        self.fa.attention(self.q, self.k, self.v, causal=self.causal, out=self.o, lse=self.lse)
+
+
+class Decode:
+    def __init__(self, fa, name="c5_decode", num_splits=0):
+        import torch
+        c = ai.CONFIGS[name]
+        self.fa = fa
+        self.B, self.Hq, self.Hkv, self.Lcap, self.d, self.dtype = c["B"], c["Hq"], c["Hkv"], c["Lcap"], c["d"], c["dtype"]
+        t0 = time.time()
+        self.lens = ai.decode_lengths(c["seed"], self.B, c["len_lo"], c["len_hi"])
+        x = ai.decode_inputs(c["seed"], self.B, self.Hq, self.Hkv, self.Lcap, self.d, self.dtype, self.lens)
+        self.q = to_dev(x["q"], self.dtype)
+        self.kc = to_dev(x["k_cache"], self.dtype)
+        self.vc = to_dev(x["v_cache"], self.dtype)
+        del x
+        self.seqlens = torch.from_numpy(self.lens).cuda()
+        self.num_splits = num_splits
+        ws = fa.fa_decode_workspace_bytes(self.B, self.Hq, self.Hkv, self.Lcap, self.d, num_splits)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((self.B, self.Hq), dtype=torch.float32, device="cuda")
+        self.bytes = decode_bytes(self.lens, self.Hq, self.Hkv, self.d)
+        self.flops = 4.0 * float(self.lens.sum()) * self.Hq * self.d
+        log(f"[bench] decode: inputs ready in {time.time() - t0:.1f}s, sum(len)={int(self.lens.sum())}, "
+            f"workspace {ws / 2**20:.1f} MiB")
+
+    def __call__(self):
+        self.fa.decode(self.q, self.kc, self.vc, self.seqlens, num_splits=self.num_splits,
+                       workspace=self.ws, out=self.o, lse=self.lse)
+
+
+def time_steps(parts, steps, warmup):
+    """Warm up, then time exactly `steps` steps; per-part event timings."""
+    import torch
+    for _ in range(warmup):
+        for p in parts:
+            p()
+    torch.cuda.synchronize()
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in parts]
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for i, p in enumerate(parts):
+            evs[s][i][0].record()
+            p()
+            evs[s][i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [[evs[s][i][0].elapsed_time(evs[s][i][1]) for s in range(steps)] for i in range(len(parts))]
+    return wall, per
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_cores_used():
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            return min(cores, max(blas))
+    except Exception:
+        pass
+    return cores
+
+
+def cpu_baseline_prefill(name="c3_llama3_8b_gqa", heads=8):
+    """The oracle on `heads` full heads of the prefill workload (all query rows,
+    all keys, causal): TFLOP/s by the same FLOP convention as the GPU."""
+    import oracle
+    c = ai.CONFIGS[name]
+    N, d, dt, grp = c["N"], c["d"], c["dtype"], c["Hq"] // c["Hkv"]
+    scale = 1.0 / math.sqrt(d)
+    elapsed = 0.0
+    for h in range(heads):
+        g = h // grp
+        q = ai.bits_to_f64(ai.slab(c["seed"], ai.Q_ID, 0, h, N, d, dt), dt)
+        k = ai.bits_to_f64(ai.slab(c["seed"], ai.K_ID, 0, g, N, d, dt), dt)
+        v = ai.bits_to_f64(ai.slab(c["seed"], ai.V_ID, 0, g, N, d, dt), dt)
+        t0 = time.perf_counter()
+        oracle.attention_head(q, k, v, scale, causal=True)
+        elapsed += time.perf_counter() - t0
+    flops = prefill_flops(1, heads, N, N, d, True)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cpu_cores_used(), "kind": "oracle",
+            "sample": f"{heads} of 32 q-heads of the N=8192 causal layer, all 8192 query rows each "
+                      f"(float64 NumPy, score matrix materialised); {elapsed:.1f}s"}
+
+
+def cpu_baseline_decode(name="c5_decode", seqs=32):
+    import oracle
+    c = ai.CONFIGS[name]
+    lens = ai.decode_lengths(c["seed"], c["B"], c["len_lo"], c["len_hi"])[:seqs]
+    Hq, Hkv, d, dt = c["Hq"], c["Hkv"], c["d"], c["dtype"]
+    elapsed = 0.0
+    for b in range(seqs):
+        L = int(lens[b])
+        q = np.stack([ai.bits_to_f64(ai.slab(c["seed"], ai.Q_ID, b, h, 1, d, dt), dt)[0] for h in range(Hq)])[None]
+        kc = np.stack([ai.bits_to_f64(ai.slab(c["seed"], ai.K_ID, b, g, L, d, dt), dt) for g in range(Hkv)])[None]
+        vc = np.stack([ai.bits_to_f64(ai.slab(c["seed"], ai.V_ID, b, g, L, d, dt), dt) for g in range(Hkv)])[None]
+        t0 = time.perf_counter()
+        oracle.decode(q, kc, vc, [L], 1.0 / math.sqrt(d))
+        elapsed += time.perf_counter() - t0
+    nbytes = decode_bytes(lens, Hq, Hkv, d)
+    return {"value": nbytes / elapsed / 1e9, "unit": "GB/s", "cores": cpu_cores_used(), "kind": "oracle",
+            "sample": f"first {seqs} of 32 sequences (lengths {lens.tolist()}), all 32 q-heads; {elapsed:.1f}s"}
+
+
+# ------------------------------------------------------------------ modes
+def calibrate_copy(nbytes=1 << 30, reps=5):
+    """A plain device-to-device copy of known size, for counter calibration."""
+    import torch
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "calibrate_copy", "bytes_read_per_copy": nbytes, "bytes_written_per_copy": nbytes,
+                      "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="default")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this path has no multi-GPU mode; "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+
+    import exact_tiled_attention_fwd_amd as fa
+    fa.load_library()
+
+    cfg = args.config
+    run_prefill = cfg in ("default", "c1_tiny_mha", "c2_mid_mha", "c2_mid_mha_causal", "c3_llama3_8b_gqa", "c4_long_context")
+    run_decode = cfg in ("default", "c5_decode")
+    if not (run_prefill or run_decode):
+        raise SystemExit(f"unknown --config {cfg}")
+    pname = "c3_llama3_8b_gqa" if cfg == "default" else cfg.replace("_causal", "")
+    causal = cfg in ("default", "c3_llama3_8b_gqa", "c4_long_context", "c2_mid_mha_causal")
+    parts = []
+    pre = dec = None
+    if run_prefill:
+        pre = Prefill(fa, pname, causal)
+        parts.append(pre)
+    if run_decode:
+        dec = Decode(fa, num_splits=args.num_splits)
+        parts.append(dec)
+
+    wall, per = time_steps(parts, args.steps, args.warmup)
+    ms_per_step = wall * 1e3 / args.steps
+    out = {"metric": "attn fwd TFLOP/s & % MFMA peak, Llama-3-8B GQA causal N=8192; decode GB/s"}
+    i = 0
+    if pre is not None:
+        t_ms = float(np.mean(per[i]))
+        tflops = pre.flops / (t_ms * 1e-3) / 1e12
+        out.update(value=round(tflops, 2), unit="TFLOP/s")
+        out["prefill"] = {"workload": f"{pname} causal={causal}", "ms_mean": round(t_ms, 4),
+                          "ms_min": round(float(np.min(per[i])), 4), "tflops": round(tflops, 2),
+                          "frac_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS, 4)}
+        traffic = counter_traffic(f"fa_fwd_{pname}_counters.md") if causal else None
+        out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
+                           "algorithmic_bytes": pre.bytes, "flops_per_launch": pre.flops}
+        i += 1
+    if dec is not None:
+        t_ms = float(np.mean(per[i]))
+        gbs = dec.bytes / (t_ms * 1e-3) / 1e9
+        droof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic("fa_decode_c5_counters.md"),
+                 "algorithmic_bytes": dec.bytes}
+        out["decode"] = {"workload": "c5_decode", "ms_mean": round(t_ms, 4), "ms_min": round(float(np.min(per[i])), 4),
+                         "value": round(gbs, 1), "unit": "GB/s", "roofline": droof}
+        if pre is None:
+            out.update(value=round(gbs, 1), unit="GB/s", roofline=droof)
+    out.update({
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if cfg != "c2_mid_mha" and cfg != "c2_mid_mha_causal" else "fp16",
+        "data": "synthetic: seeded N(0,1) rounded to bf16/fp16",
+        "config": {"workload": "c3 prefill (B=1,Hq=32,Hkv=8,N=8192,d=128,causal) + c5 decode (32 seq, Hq=32,Hkv=8,d=128, L~U[1024,32768])"
+                   if cfg == "default" else cfg,
+                   "kernel_source_sha256": kernel_source_hash()},
+    })
+    if not args.no_cpu_baseline:
+        if pre is not None and pname == "c3_llama3_8b_gqa":
+            out["cpu_baseline"] = cpu_baseline_prefill()
+            if dec is not None:
+                out["decode"]["cpu_baseline"] = cpu_baseline_decode()
+        elif dec is not None:
+            out["cpu_baseline"] = cpu_baseline_decode()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -89,28 +89,10 @@ __global__ __launch_bounds__(kThreads, 1) void fa_decode_split_kernel(
         for (int r = 0; r < 16; ++r)
           if (jw + acc_key(r, half) >= n) s_acc[r] = -__builtin_inff();
       }
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_acc[r]);
-      mx = halves_max(mx);
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      float psum = 0.f;
-      uint32_t pk[8];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = exp2_fast(__builtin_fmaf(s_acc[r], scale_log2, -m_use));
-        const float p1 = exp2_fast(__builtin_fmaf(s_acc[r + 1], scale_log2, -m_use));
-        psum += p0 + p1;
-        pk[r >> 1] = pack2<DT>(p0, p1);
-      }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int mt = 0; mt < T::MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
+      f32x16 s1[1] = {s_acc};
+      uint32_t pk1[1][8];
+      softmax_step<DT, 1, T::MT>(s1, scale_log2, m_run, l_run, acc_o, pk1);
+      const uint32_t* pk = pk1[0];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const u32x4 bop = {pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]};

@@ -126,15 +126,16 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(
     const char* st = smem + (jt & 1) * T::STAGE_BYTES;
 
     if (wave_active && jt < wave_tiles) {
-      // ---- S^T = K Q^T
+      // ---- S^T = K Q^T (the two 32-key blocks interleaved: independent chains)
       f32x16 s[T::KB];
 #pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb) {
+      for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < T::KS; ++ks) s[kb] = mfma32<DT>(k_operand<D, ROWS>(st, kb, ks, lane), qop[ks], s[kb]);
-      }
+      for (int ks = 0; ks < T::KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < T::KB; ++kb) s[kb] = mfma32<DT>(k_operand<D, ROWS>(st, kb, ks, lane), qop[ks], s[kb]);
       // ---- mask: ragged key tail, causal diagonal
       const bool need_mask = (j0 + ROWS > Nk) || (CAUSAL && j0 + ROWS - 1 > q0w + off);
       if (need_mask) {
@@ -146,32 +147,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(
             if (j0 + 32 * kb + acc_key(r, half) >= lim) s[kb][r] = -__builtin_inff();
       }
       // ---- online softmax (base 2)
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = halves_max(mx);
-      const float m_new = fmaxf(m_run, mx * scale_log2);
-      const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_run - m_use);
-      float psum = 0.f;
       uint32_t pk[T::KB][8];
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = exp2_fast(__builtin_fmaf(s[kb][r], scale_log2, -m_use));
-          const float p1 = exp2_fast(__builtin_fmaf(s[kb][r + 1], scale_log2, -m_use));
-          psum += p0 + p1;
-          pk[kb][r >> 1] = pack2<DT>(p0, p1);
-        }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int mt = 0; mt < T::MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
+      softmax_step<DT, T::KB, T::MT>(s, scale_log2, m_run, l_run, acc_o, pk);
       // ---- O^T += V^T P^T
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb)

@@ -64,14 +64,25 @@ struct Tile {
 };
 
 // ------------------------------------------------------------------ HBM -> regs
-// Thread t moves U units; unit = 4 consecutive rows x one 16-byte chunk. Within
-// a wave the 64 lanes cover 16 row-quads x 4 chunks, which keeps the global
-// loads in 64-byte runs per row and the transposed LDS writes conflict-free.
+// K moves in 16-byte chunks in row-major order (a wave covers 64 consecutive
+// chunks: fully coalesced loads, and each 16-lane group writes one LDS row).
+// V moves in units of 4 consecutive rows x one 16-byte chunk, which is what
+// the transposed LDS layout needs; within a wave the 64 lanes cover 16
+// row-quads x 4 chunks, which keeps the transposed LDS writes conflict-free.
 template <int D, int ROWS>
 struct TileRegs {
-  u32x4 k[Tile<D, ROWS>::U][4];
+  static constexpr int KU = ROWS * (D / 8) / 256;  // K chunks per thread
+  u32x4 k[KU];
   u32x4 v[Tile<D, ROWS>::U][4];
 };
+
+template <int D, int ROWS>
+__device__ inline void k_coords(int p, int& row, int& c) {
+  constexpr int CPR = D / 8;
+  const int idx = threadIdx.x + 256 * p;
+  row = idx / CPR;
+  c = idx % CPR;
+}
 
 template <int D, int ROWS>
 __device__ inline void unit_coords(int p, int& kq, int& c) {
@@ -83,25 +94,30 @@ __device__ inline void unit_coords(int p, int& kq, int& c) {
 }
 
 // Load rows [0, nvalid) of a tile whose first row is at kbase/vbase (row
-// stride D elements). Rows at or beyond nvalid are zero-filled and never read.
+// stride D elements), nvalid >= 1. Rows at or beyond nvalid re-read row
+// nvalid-1: their scores are masked to -inf, so they contribute exactly 0,
+// and no row past the valid range is ever touched.
 template <int D, int ROWS>
 __device__ inline void load_tile(const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase,
                                  int nvalid, TileRegs<D, ROWS>& r) {
+  using R = TileRegs<D, ROWS>;
+  const bool full = nvalid >= ROWS;
+#pragma unroll
+  for (int p = 0; p < R::KU; ++p) {
+    int row, c;
+    k_coords<D, ROWS>(p, row, c);
+    if (!full) row = min(row, nvalid - 1);
+    r.k[p] = *reinterpret_cast<const u32x4*>(kbase + (size_t)row * D + (size_t)c * 8);
+  }
 #pragma unroll
   for (int p = 0; p < Tile<D, ROWS>::U; ++p) {
     int kq, c;
     unit_coords<D, ROWS>(p, kq, c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = 4 * kq + i;
-      if (row < nvalid) {
-        const size_t off = (size_t)row * D + (size_t)c * 8;
-        r.k[p][i] = *reinterpret_cast<const u32x4*>(kbase + off);
-        r.v[p][i] = *reinterpret_cast<const u32x4*>(vbase + off);
-      } else {
-        r.k[p][i] = u32x4{0u, 0u, 0u, 0u};
-        r.v[p][i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      int row = 4 * kq + i;
+      if (!full) row = min(row, nvalid - 1);
+      r.v[p][i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)row * D + (size_t)c * 8);
     }
   }
 }
@@ -121,14 +137,15 @@ __device__ inline void store_tile(char* __restrict__ stage, const TileRegs<D, RO
   char* kl = stage;
   char* vl = stage + T::K_BYTES;
 #pragma unroll
+  for (int p = 0; p < TileRegs<D, ROWS>::KU; ++p) {
+    int row, c;
+    k_coords<D, ROWS>(p, row, c);
+    *reinterpret_cast<u32x4*>(kl + row * (D * 2) + ((c ^ T::swz(row)) * 16)) = r.k[p];
+  }
+#pragma unroll
   for (int p = 0; p < T::U; ++p) {
     int kq, c;
     unit_coords<D, ROWS>(p, kq, c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 4 * kq + i;
-      *reinterpret_cast<u32x4*>(kl + row * (D * 2) + ((c ^ T::swz(row)) * 16)) = r.k[p][i];
-    }
     // V^T: 8 head-dim rows, each gets the 4 keys of this row-quad (8 bytes).
     const int grp = kq >> 2;
     const int pos = 16 * grp + 4 * vt_quad_pos(kq & 3);
@@ -197,5 +214,52 @@ __device__ inline float halves_sum(float x) {
 
 // Key offset (within a 32-key block) of accumulator register r in lane half h.
 __device__ inline int acc_key(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Rescale threshold, log2 units. The reference point m of a row (the value
+// subtracted before exponentiating) only moves up when a tile's maximum
+// exceeds it by more than this; exp(m_old - m_new) is then applied to the
+// running sum and the output accumulator. Any reference point gives the same
+// exact result (the merge identity of "The math of Flash Attention",
+// unite.ai, holds for any common shift); this one keeps every p <= 2^8 and
+// lets most tiles skip the rescale.
+constexpr float kRescaleLog2 = 8.f;
+
+// One online-softmax step over NS 32-key blocks of S^T (raw scores, masked
+// entries -inf). c = scale*log2(e). Updates the row reference m_run (log2
+// units, per lane = per query column), this lane's share of the running sum
+// l_run, rescales acc_o when m_run moves, and returns P rounded to the input
+// type, packed two per register in accumulator order.
+template <int DT, int NS, int MT>
+__device__ inline void softmax_step(f32x16 (&s)[NS], float c, float& m_run, float& l_run, f32x16 (&acc_o)[MT],
+                                    uint32_t (&pk)[NS][8]) {
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int kb = 0; kb < NS; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  mx = halves_max(mx) * c;
+  if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_new == -__builtin_inff()) ? 1.f : exp2_fast(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
+  float psum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < NS; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = exp2_fast(__builtin_fmaf(s[kb][r], c, -m_use));
+      const float p1 = exp2_fast(__builtin_fmaf(s[kb][r + 1], c, -m_use));
+      psum += p0 + p1;
+      pk[kb][r >> 1] = pack2<DT>(p0, p1);
+    }
+  l_run += psum;
+}
 
 }  // namespace fa
