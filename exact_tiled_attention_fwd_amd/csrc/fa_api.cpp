@@ -136,7 +136,8 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   size_t qb, kb, lb;
   if (!mul_bytes(qb, {B, Hq, Nq, d, 2}) || !mul_bytes(kb, {B, Hkv, Nk, d, 2}) || !mul_bytes(lb, {B, Hq, Nq, 4}))
     return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
-  if ((long long)((Nq + 127) / 128) * B * Hq > 0x7fffffffLL) return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  if ((long long)((Nq + fa::kFwdBlockRows - 1) / fa::kFwdBlockRows) * B * Hq > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "grid too large");
   if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb))
     return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
   if (lse && (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) || overlap(lse, lb, o, qb)))

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_decode_split_kernel(
         const u32x4 bop = {pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]};
 #pragma unroll
         for (int mt = 0; mt < T::MT; ++mt)
-          acc_o[mt] = mfma32<DT>(vt_operand<D, kRows>(st, mt, 2 * wave + u, lane), bop, acc_o[mt]);
+          acc_o[mt] = mfma32<DT>(vt_operand<D, kRows>(st + T::K_BYTES, mt, 2 * wave + u, lane), bop, acc_o[mt]);
       }
     }
     if (more) store_tile<D, kRows>(smem + ((jt + 1) & 1) * T::STAGE_BYTES, regs);

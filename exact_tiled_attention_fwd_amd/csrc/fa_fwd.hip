@@ -1,19 +1,22 @@
 // fa_fwd.hip - prefill attention forward for gfx950.
 //
-// One workgroup (4 waves) owns BM = 128 query rows of one (batch, q-head); each
-// wave owns 32 of them. The workgroup walks the key/value tiles of its kv-head
-// (an outer loop over query blocks and an inner loop over key/value blocks, as
-// in "Implementation details" of "Flash Attention: Revolutionizing Transformer
-// Efficiency", unite.ai), streaming each tile HBM -> registers -> LDS with a
-// double buffer so the next tile's loads are in flight while the current tile
-// is multiplied. Per tile and wave:
-//   S^T = K Q^T on the matrix cores (fp32 accumulate),
-//   online softmax in base 2 (running max m, running sum l; the merge identity
-//   of "The math of Flash Attention" on the same page),
-//   O^T += V^T P^T with P rounded to the input type.
-// O is divided by l once after the last tile and written once, with the
-// natural-log LSE. Causal key tiles entirely above the diagonal are never
-// loaded (SDPA page, devhandbook.co.kr, Example 3, is_causal).
+// One workgroup owns BM = 256 query rows of one (batch, q-head): 8 waves of 32
+// rows each, in two groups of 4. The workgroup walks the key/value tiles of
+// its kv-head (an outer loop over query blocks and an inner loop over
+// key/value blocks, as in "Implementation details" of "Flash Attention:
+// Revolutionizing Transformer Efficiency", unite.ai). Per tile and wave:
+//   MA: S^T = K Q^T on the matrix cores (fp32 accumulate),
+//   SM: online softmax in base 2 (running max m, running sum l; the merge
+//       identity of "The math of Flash Attention" on the same page),
+//   MB: O^T += V^T P^T with P rounded to the input type.
+// The two groups run out of phase: while one group's waves issue matrix-core
+// work (MB of the previous tile and MA of the current one), the other group's
+// waves, which share the same SIMDs, run their softmax on the vector ALUs.
+// Each phase ends at a workgroup barrier. Group 0 streams the V tiles and
+// group 1 the K tiles HBM -> registers -> LDS, one tile ahead, into a 2-deep
+// ring for each. O is divided by l once after the last tile and written
+// once, with the natural-log LSE. Causal key tiles entirely above the
+// diagonal are never loaded (SDPA page, devhandbook.co.kr, Example 3).
 #include "fa_launch.h"
 #include "fa_tile.h"
 
@@ -21,8 +24,8 @@ namespace fa {
 
 namespace {
 
-constexpr int kBM = 128;      // query rows per workgroup
-constexpr int kThreads = 256; // 4 waves
+constexpr int kBM = kFwdBlockRows;  // query rows per workgroup
+constexpr int kThreads = 512;  // 8 waves = 2 groups of 4
 
 // Work item of a workgroup: (b, kv-head g, q-head h, query tile qt).
 struct Work {
@@ -61,16 +64,20 @@ __device__ inline Work map_work(int L, int B, int Hq, int Hkv, int n_qt) {
 }
 
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(
+__global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Nq, int Nk,
     float scale_log2, int n_qt) {
   constexpr int ROWS = 8192 / D;  // keys per tile: 64 (d=128) or 128 (d=64)
   using T = Tile<D, ROWS>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[2 * T::K_BYTES + 2 * T::VT_BYTES];
+  char* const kring = smem;                    // K tiles, slot = tile & 1
+  char* const vring = smem + 2 * T::K_BYTES;   // V^T tiles, slot = tile & 1
 
   const Work wk = map_work(blockIdx.x, B, Hq, Hkv, n_qt);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
+  const int grp = wave >> 2;                // 0: V loader, MFMA first; 1: K loader
+  const int gtid = threadIdx.x & 255;       // thread index within the group
   const int q0 = wk.qt * kBM;
   const int q0w = q0 + 32 * wave;  // first query row of this wave
   const int off = Nk - Nq;         // causal: key j visible to query i iff j <= i + off
@@ -87,9 +94,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(
     const int last_key = min(q0 + kBM, Nq) - 1 + off;
     n_kv = min(n_kv, last_key / ROWS + 1);
   }
-  // Key tiles this wave computes on.
+  // Key tiles this wave computes on (0 if the wave has no valid query row).
   const bool wave_active = q0w < Nq;
-  int wave_tiles = n_kv;
+  int wave_tiles = wave_active ? n_kv : 0;
   if (CAUSAL && wave_active) wave_tiles = min(n_kv, (min(q0w + 31, Nq - 1) + off) / ROWS + 1);
 
   // Q^T operand (B operand of S^T = K Q^T), held for the whole loop.
@@ -97,7 +104,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(
   u32x4 qop[T::KS];
 #pragma unroll
   for (int ks = 0; ks < T::KS; ++ks) {
-    if (wave_active && qrow < Nq)
+    if (qrow < Nq)
       qop[ks] = *reinterpret_cast<const u32x4*>(qp + (size_t)qrow * D + 16 * ks + 8 * half);
     else
       qop[ks] = u32x4{0u, 0u, 0u, 0u};
@@ -108,61 +115,73 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_kernel(
   for (int mt = 0; mt < T::MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[mt][r] = 0.f;
-  float m_run = -__builtin_inff();  // running max of scaled scores, log2 units
+  float m_run = -__builtin_inff();  // row reference point, log2 units
   float l_run = 0.f;                // this lane's share of the running sum
+  f32x16 s[T::KB];                  // S^T of the tile last multiplied
+  uint32_t pk[T::KB][8];            // P of the tile last softmaxed
 
-  TileRegs<D, ROWS> regs;
-  load_tile<D, ROWS>(kp, vp, min(ROWS, Nk), regs);
-  store_tile<D, ROWS>(smem, regs);
-  __syncthreads();
-
-  for (int jt = 0; jt < n_kv; ++jt) {
-    const int j0 = jt * ROWS;
-    const bool more = jt + 1 < n_kv;
-    if (more) {
-      const int jn = j0 + ROWS;
-      load_tile<D, ROWS>(kp + (size_t)jn * D, vp + (size_t)jn * D, min(ROWS, Nk - jn), regs);
-    }
-    const char* st = smem + (jt & 1) * T::STAGE_BYTES;
-
-    if (wave_active && jt < wave_tiles) {
-      // ---- S^T = K Q^T (the two 32-key blocks interleaved: independent chains)
-      f32x16 s[T::KB];
+  // SM(j): mask the ragged key tail / causal diagonal, online softmax -> pk.
+  auto softmax = [&](int j) {
+    const int j0 = j * ROWS;
+    const bool need_mask = (j0 + ROWS > Nk) || (CAUSAL && j0 + ROWS - 1 > q0w + off);
+    if (need_mask) {
+      const int lim = CAUSAL ? min(Nk, qrow + off + 1) : Nk;  // keys < lim are visible
 #pragma unroll
       for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < T::KS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < T::KB; ++kb) s[kb] = mfma32<DT>(k_operand<D, ROWS>(st, kb, ks, lane), qop[ks], s[kb]);
-      // ---- mask: ragged key tail, causal diagonal
-      const bool need_mask = (j0 + ROWS > Nk) || (CAUSAL && j0 + ROWS - 1 > q0w + off);
-      if (need_mask) {
-        const int lim = CAUSAL ? min(Nk, qrow + off + 1) : Nk;  // keys < lim are visible
-#pragma unroll
-        for (int kb = 0; kb < T::KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (j0 + 32 * kb + acc_key(r, half) >= lim) s[kb][r] = -__builtin_inff();
-      }
-      // ---- online softmax (base 2)
-      uint32_t pk[T::KB][8];
-      softmax_step<DT, T::KB, T::MT>(s, scale_log2, m_run, l_run, acc_o, pk);
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const u32x4 b = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
-#pragma unroll
-          for (int mt = 0; mt < T::MT; ++mt)
-            acc_o[mt] = mfma32<DT>(vt_operand<D, ROWS>(st, mt, 2 * kb + u, lane), b, acc_o[mt]);
-        }
+        for (int r = 0; r < 16; ++r)
+          if (j0 + 32 * kb + acc_key(r, half) >= lim) s[kb][r] = -__builtin_inff();
     }
+    softmax_step<DT, T::KB, T::MT>(s, scale_log2, m_run, l_run, acc_o, pk);
+  };
+  // Matrix-core phase: MB(jo) = O^T += V^T_jo P^T (if do_o), MA(js) = S^T = K_js Q^T (if do_s).
+  auto mma = [&](bool do_o, int jo, bool do_s, int js) {
+    const char* vl = vring + (jo & 1) * T::VT_BYTES;
+    const char* kl = kring + (js & 1) * T::K_BYTES;
+    if (do_o && do_s)
+      mma_phase<DT, D, ROWS, true, true>(vl, kl, pk, qop, acc_o, s, lane);
+    else if (do_o)
+      mma_phase<DT, D, ROWS, true, false>(vl, kl, pk, qop, acc_o, s, lane);
+    else if (do_s)
+      mma_phase<DT, D, ROWS, false, true>(vl, kl, pk, qop, acc_o, s, lane);
+  };
+  auto tile_rows = [&](int j) { return min(ROWS, Nk - j * ROWS); };
 
-    if (more) store_tile<D, ROWS>(smem + ((jt + 1) & 1) * T::STAGE_BYTES, regs);
+  // Each group runs its own loop (both execute the same number of barriers):
+  // macro-step i is phase A then phase B, each closed by a barrier.
+  //   group 0: A = store V_i, load V_{i+1}, MB(i-1), MA(i)   B = SM(i)
+  //   group 1: A = load K_{i+1}, SM(i-1)                     B = MB(i-1), MA(i), store K_{i+1}
+  // V_i / K_i live in ring slot i & 1; a slot is rewritten only after the
+  // barrier that ends the last phase reading its previous tile.
+  if (grp == 0) {
+    u32x4 rv[T::U][4];
+    load_v<D, ROWS>(vp, tile_rows(0), gtid, rv);
+    store_v<D, ROWS>(vring, gtid, rv);
+    if (n_kv > 1) load_v<D, ROWS>(vp + (size_t)ROWS * D, tile_rows(1), gtid, rv);
     __syncthreads();
+    for (int i = 0; i <= n_kv; ++i) {
+      if (i >= 1 && i < n_kv) {
+        store_v<D, ROWS>(vring + (i & 1) * T::VT_BYTES, gtid, rv);
+        if (i + 1 < n_kv) load_v<D, ROWS>(vp + (size_t)(i + 1) * ROWS * D, tile_rows(i + 1), gtid, rv);
+      }
+      mma(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
+      __syncthreads();
+      if (i < wave_tiles) softmax(i);
+      __syncthreads();
+    }
+  } else {
+    u32x4 rk[TileRegs<D, ROWS>::KU];
+    load_k<D, ROWS>(kp, tile_rows(0), gtid, rk);
+    store_k<D, ROWS>(kring, gtid, rk);
+    __syncthreads();
+    for (int i = 0; i <= n_kv; ++i) {
+      if (i + 1 < n_kv) load_k<D, ROWS>(kp + (size_t)(i + 1) * ROWS * D, tile_rows(i + 1), gtid, rk);
+      if (i >= 1 && i - 1 < wave_tiles) softmax(i - 1);
+      __syncthreads();
+      mma(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
+      if (i + 1 < n_kv) store_k<D, ROWS>(kring + ((i + 1) & 1) * T::K_BYTES, gtid, rk);
+      __syncthreads();
+    }
   }
 
   if (!wave_active) return;

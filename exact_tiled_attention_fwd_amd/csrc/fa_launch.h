@@ -44,6 +44,7 @@ struct DecodeArgs {
 };
 
 constexpr int kDecodeTileRows = 128;
+constexpr int kFwdBlockRows = 256;  // query rows per prefill workgroup
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

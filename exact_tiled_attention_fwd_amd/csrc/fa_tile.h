@@ -77,49 +77,61 @@ struct TileRegs {
 };
 
 template <int D, int ROWS>
-__device__ inline void k_coords(int p, int& row, int& c) {
+__device__ inline void k_coords(int tid, int p, int& row, int& c) {
   constexpr int CPR = D / 8;
-  const int idx = threadIdx.x + 256 * p;
+  const int idx = tid + 256 * p;
   row = idx / CPR;
   c = idx % CPR;
 }
 
 template <int D, int ROWS>
-__device__ inline void unit_coords(int p, int& kq, int& c) {
+__device__ inline void unit_coords(int tid, int p, int& kq, int& c) {
   constexpr int CG = Tile<D, ROWS>::CPR / 4;  // chunk groups per row
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = tid >> 6, lane = tid & 63;
   const int wu = w + 4 * p;
   kq = 16 * (wu / CG) + (lane & 15);
   c = 4 * (wu % CG) + (lane >> 4);
 }
 
-// Load rows [0, nvalid) of a tile whose first row is at kbase/vbase (row
-// stride D elements), nvalid >= 1. Rows at or beyond nvalid re-read row
-// nvalid-1: their scores are masked to -inf, so they contribute exactly 0,
-// and no row past the valid range is ever touched.
+// Loads of one tile by a group of 256 threads (tid in [0, 256)). Rows
+// [0, nvalid) of the tile are valid, nvalid >= 1; rows at or beyond nvalid
+// re-read row nvalid-1: their scores are masked to -inf, so they contribute
+// exactly 0, and no row past the valid range is ever touched.
 template <int D, int ROWS>
-__device__ inline void load_tile(const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase,
-                                 int nvalid, TileRegs<D, ROWS>& r) {
-  using R = TileRegs<D, ROWS>;
+__device__ inline void load_k(const uint16_t* __restrict__ kbase, int nvalid, int tid,
+                              u32x4 (&rk)[TileRegs<D, ROWS>::KU]) {
   const bool full = nvalid >= ROWS;
 #pragma unroll
-  for (int p = 0; p < R::KU; ++p) {
+  for (int p = 0; p < TileRegs<D, ROWS>::KU; ++p) {
     int row, c;
-    k_coords<D, ROWS>(p, row, c);
+    k_coords<D, ROWS>(tid, p, row, c);
     if (!full) row = min(row, nvalid - 1);
-    r.k[p] = *reinterpret_cast<const u32x4*>(kbase + (size_t)row * D + (size_t)c * 8);
+    rk[p] = *reinterpret_cast<const u32x4*>(kbase + (size_t)row * D + (size_t)c * 8);
   }
+}
+
+template <int D, int ROWS>
+__device__ inline void load_v(const uint16_t* __restrict__ vbase, int nvalid, int tid,
+                              u32x4 (&rv)[Tile<D, ROWS>::U][4]) {
+  const bool full = nvalid >= ROWS;
 #pragma unroll
   for (int p = 0; p < Tile<D, ROWS>::U; ++p) {
     int kq, c;
-    unit_coords<D, ROWS>(p, kq, c);
+    unit_coords<D, ROWS>(tid, p, kq, c);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int row = 4 * kq + i;
       if (!full) row = min(row, nvalid - 1);
-      r.v[p][i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)row * D + (size_t)c * 8);
+      rv[p][i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)row * D + (size_t)c * 8);
     }
   }
+}
+
+template <int D, int ROWS>
+__device__ inline void load_tile(const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase,
+                                 int nvalid, TileRegs<D, ROWS>& r) {
+  load_k<D, ROWS>(kbase, nvalid, threadIdx.x, r.k);
+  load_v<D, ROWS>(vbase, nvalid, threadIdx.x, r.v);
 }
 
 // Position (in elements) of key kk (0..15) inside its 16-key group of V^T: the
@@ -132,26 +144,29 @@ __device__ inline int vt_quad_pos(int quad) {  // quad = kk/4 in 0..3
 
 // ------------------------------------------------------------------ regs -> LDS
 template <int D, int ROWS>
-__device__ inline void store_tile(char* __restrict__ stage, const TileRegs<D, ROWS>& r) {
+__device__ inline void store_k(char* __restrict__ kl, int tid, const u32x4 (&rk)[TileRegs<D, ROWS>::KU]) {
   using T = Tile<D, ROWS>;
-  char* kl = stage;
-  char* vl = stage + T::K_BYTES;
 #pragma unroll
   for (int p = 0; p < TileRegs<D, ROWS>::KU; ++p) {
     int row, c;
-    k_coords<D, ROWS>(p, row, c);
-    *reinterpret_cast<u32x4*>(kl + row * (D * 2) + ((c ^ T::swz(row)) * 16)) = r.k[p];
+    k_coords<D, ROWS>(tid, p, row, c);
+    *reinterpret_cast<u32x4*>(kl + row * (D * 2) + ((c ^ T::swz(row)) * 16)) = rk[p];
   }
+}
+
+// V^T: each unit covers 8 head-dim rows x the 4 keys of its row-quad (8 bytes).
+template <int D, int ROWS>
+__device__ inline void store_v(char* __restrict__ vl, int tid, const u32x4 (&rv)[Tile<D, ROWS>::U][4]) {
+  using T = Tile<D, ROWS>;
 #pragma unroll
   for (int p = 0; p < T::U; ++p) {
     int kq, c;
-    unit_coords<D, ROWS>(p, kq, c);
-    // V^T: 8 head-dim rows, each gets the 4 keys of this row-quad (8 bytes).
+    unit_coords<D, ROWS>(tid, p, kq, c);
     const int grp = kq >> 2;
     const int pos = 16 * grp + 4 * vt_quad_pos(kq & 3);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const uint32_t a0 = r.v[p][0][t], a1 = r.v[p][1][t], a2 = r.v[p][2][t], a3 = r.v[p][3][t];
+      const uint32_t a0 = rv[p][0][t], a1 = rv[p][1][t], a2 = rv[p][2][t], a3 = rv[p][3][t];
       // element 2t (low halves) and 2t+1 (high halves) of the 4 rows
       const u32x2 even = {__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
       const u32x2 odd = {__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
@@ -162,22 +177,31 @@ __device__ inline void store_tile(char* __restrict__ stage, const TileRegs<D, RO
   }
 }
 
+// A stage holds K (K_BYTES) followed by V^T (VT_BYTES).
+template <int D, int ROWS>
+__device__ inline void store_tile(char* __restrict__ stage, const TileRegs<D, ROWS>& r) {
+  store_k<D, ROWS>(stage, threadIdx.x, r.k);
+  store_v<D, ROWS>(stage + Tile<D, ROWS>::K_BYTES, threadIdx.x, r.v);
+}
+
 // ------------------------------------------------------------------ operands
 // A operand of S^T = K Q^T: key row 32*kb + lane%32, d = 16*ks + 8*(lane/32) .. +7
+// (kl points at the K region of a stage.)
 template <int D, int ROWS>
-__device__ inline u32x4 k_operand(const char* __restrict__ stage, int kb, int ks, int lane) {
+__device__ inline u32x4 k_operand(const char* __restrict__ kl, int kb, int ks, int lane) {
   using T = Tile<D, ROWS>;
   const int row = 32 * kb + (lane & 31);
   const int chunk = 2 * ks + (lane >> 5);
-  return *reinterpret_cast<const u32x4*>(stage + row * (D * 2) + ((chunk ^ T::swz(row)) * 16));
+  return *reinterpret_cast<const u32x4*>(kl + row * (D * 2) + ((chunk ^ T::swz(row)) * 16));
 }
 
 // A operand of O^T += V^T P^T: d row 32*mt + lane%32, 16-key group G, half lane/32
+// (vl points at the V^T region of a stage.)
 template <int D, int ROWS>
-__device__ inline u32x4 vt_operand(const char* __restrict__ stage, int mt, int G, int lane) {
+__device__ inline u32x4 vt_operand(const char* __restrict__ vl, int mt, int G, int lane) {
   using T = Tile<D, ROWS>;
   const int d = 32 * mt + (lane & 31);
-  return *reinterpret_cast<const u32x4*>(stage + T::K_BYTES + d * T::VT_STRIDE + G * 32 + (lane >> 5) * 16);
+  return *reinterpret_cast<const u32x4*>(vl + d * T::VT_STRIDE + G * 32 + (lane >> 5) * 16);
 }
 
 // ------------------------------------------------------------------ MFMA
@@ -200,6 +224,60 @@ __device__ inline uint32_t pack2(float lo, float hi) {
 }
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Matrix-core phase of one wave on one tile pair: optionally O^T += V^T P^T
+// for the previous tile (DO_O) and S^T = K Q^T for the current one (DO_S).
+// The A operands come from LDS; they are fetched PF MFMAs ahead through a
+// small register ring so LDS latency hides under the matrix-core work, and
+// consecutive MFMAs use different accumulators.
+template <int DT, int D, int ROWS, bool DO_O, bool DO_S>
+__device__ inline void mma_phase(const char* __restrict__ vl, const char* __restrict__ kl,
+                                 const uint32_t (&pk)[ROWS / 32][8], const u32x4 (&qop)[D / 16],
+                                 f32x16 (&acc_o)[D / 32], f32x16 (&s)[ROWS / 32], int lane) {
+  using T = Tile<D, ROWS>;
+  constexpr int NO = DO_O ? T::KB * 2 * T::MT : 0;
+  constexpr int NS = DO_S ? T::KS * T::KB : 0;
+  constexpr int N = NO + NS;
+  constexpr int PF = 4;
+  static_assert(N >= PF, "pipeline depth");
+  if constexpr (DO_S) {
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+  }
+  auto rd = [&](int t) -> u32x4 {
+    if (t < NO) {
+      const int kb = t / (2 * T::MT), u = (t / T::MT) % 2, mt = t % T::MT;
+      return vt_operand<D, ROWS>(vl, mt, 2 * kb + u, lane);
+    }
+    const int t2 = t - NO, ks = t2 / T::KB, kb = t2 % T::KB;
+    return k_operand<D, ROWS>(kl, kb, ks, lane);
+  };
+  u32x4 buf[PF];
+#pragma unroll
+  for (int t = 0; t < PF; ++t) buf[t] = rd(t);
+#pragma unroll
+  for (int t = 0; t < N; ++t) {
+    const u32x4 a = buf[t % PF];
+    if (t + PF < N) buf[t % PF] = rd(t + PF);
+    if (t < NO) {
+      const int kb = t / (2 * T::MT), u = (t / T::MT) % 2, mt = t % T::MT;
+      const u32x4 b = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
+      acc_o[mt] = mfma32<DT>(a, b, acc_o[mt]);
+    } else {
+      const int t2 = t - NO, ks = t2 / T::KB, kb = t2 % T::KB;
+      s[kb] = mfma32<DT>(a, qop[ks], s[kb]);
+    }
+  }
+  // Keep the issue order: PF reads, then (MFMA, read) pairs, then the tail.
+  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+  for (int t = 0; t < N; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (t + PF < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
 
 // max / sum of x over lanes l and l^32. v_permlane32_swap(x, x) returns, in
 // every lane, the pair {x[l & 31], x[(l & 31) + 32]}.
