@@ -135,15 +135,27 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
     softmax_step<DT, T::KB, T::MT>(s, scale_log2, m_run, l_run, acc_o, pk);
   };
   // Matrix-core phase: MB(jo) = O^T += V^T_jo P^T (if do_o), MA(js) = S^T = K_js Q^T (if do_s).
+  // mma_pre issues the first operand reads; mma finishes the phase.
+  u32x4 obuf[kPF];
+  auto mma_pre = [&](bool do_o, int jo, bool do_s, int js) {
+    const char* vl = vring + (jo & 1) * T::VT_BYTES;
+    const char* kl = kring + (js & 1) * T::K_BYTES;
+    if (do_o && do_s)
+      mma_prefetch<D, ROWS, true, true>(obuf, vl, kl, lane);
+    else if (do_o)
+      mma_prefetch<D, ROWS, true, false>(obuf, vl, kl, lane);
+    else if (do_s)
+      mma_prefetch<D, ROWS, false, true>(obuf, vl, kl, lane);
+  };
   auto mma = [&](bool do_o, int jo, bool do_s, int js) {
     const char* vl = vring + (jo & 1) * T::VT_BYTES;
     const char* kl = kring + (js & 1) * T::K_BYTES;
     if (do_o && do_s)
-      mma_phase<DT, D, ROWS, true, true>(vl, kl, pk, qop, acc_o, s, lane);
+      mma_run<DT, D, ROWS, true, true>(obuf, vl, kl, pk, qop, acc_o, s, lane);
     else if (do_o)
-      mma_phase<DT, D, ROWS, true, false>(vl, kl, pk, qop, acc_o, s, lane);
+      mma_run<DT, D, ROWS, true, false>(obuf, vl, kl, pk, qop, acc_o, s, lane);
     else if (do_s)
-      mma_phase<DT, D, ROWS, false, true>(vl, kl, pk, qop, acc_o, s, lane);
+      mma_run<DT, D, ROWS, false, true>(obuf, vl, kl, pk, qop, acc_o, s, lane);
   };
   auto tile_rows = [&](int j) { return min(ROWS, Nk - j * ROWS); };
 
@@ -159,6 +171,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
     store_v<D, ROWS>(vring, gtid, rv);
     if (n_kv > 1) load_v<D, ROWS>(vp + (size_t)ROWS * D, tile_rows(1), gtid, rv);
     __syncthreads();
+    mma_pre(false, -1, 0 < wave_tiles, 0);
     for (int i = 0; i <= n_kv; ++i) {
       if (i >= 1 && i < n_kv) {
         store_v<D, ROWS>(vring + (i & 1) * T::VT_BYTES, gtid, rv);
@@ -167,6 +180,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
       mma(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
       __syncthreads();
       if (i < wave_tiles) softmax(i);
+      // V_i (stored in phase A) is complete: start the next phase's reads.
+      mma_pre(i < wave_tiles, i, i + 1 < wave_tiles, i + 1);
       __syncthreads();
     }
   } else {
@@ -177,6 +192,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
     for (int i = 0; i <= n_kv; ++i) {
       if (i + 1 < n_kv) load_k<D, ROWS>(kp + (size_t)(i + 1) * ROWS * D, tile_rows(i + 1), gtid, rk);
       if (i >= 1 && i - 1 < wave_tiles) softmax(i - 1);
+      // V_{i-1} and K_i were completed before the last barrier.
+      mma_pre(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
       __syncthreads();
       mma(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
       if (i + 1 < n_kv) store_k<D, ROWS>(kring + ((i + 1) & 1) * T::K_BYTES, gtid, rk);

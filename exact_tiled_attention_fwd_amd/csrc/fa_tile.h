@@ -226,56 +226,82 @@ __device__ inline uint32_t pack2(float lo, float hi) {
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Matrix-core phase of one wave on one tile pair: optionally O^T += V^T P^T
-// for the previous tile (DO_O) and S^T = K Q^T for the current one (DO_S).
-// The A operands come from LDS; they are fetched PF MFMAs ahead through a
-// small register ring so LDS latency hides under the matrix-core work, and
-// consecutive MFMAs use different accumulators.
-template <int DT, int D, int ROWS, bool DO_O, bool DO_S>
-__device__ inline void mma_phase(const char* __restrict__ vl, const char* __restrict__ kl,
-                                 const uint32_t (&pk)[ROWS / 32][8], const u32x4 (&qop)[D / 16],
-                                 f32x16 (&acc_o)[D / 32], f32x16 (&s)[ROWS / 32], int lane) {
+// for the previous tile (DO_O) and S^T = K Q^T for the current one (DO_S),
+// the O operations first. The A operands come from LDS through a ring of
+// kPF registers, fetched kPF MFMAs ahead; mma_prefetch issues the first kPF
+// reads (it may run before the barrier that opens the phase when those tiles
+// are already complete), mma_run does the rest.
+constexpr int kPF = 4;
+
+template <int D, int ROWS, bool DO_O, bool DO_S>
+struct MmaPlan {
   using T = Tile<D, ROWS>;
-  constexpr int NO = DO_O ? T::KB * 2 * T::MT : 0;
-  constexpr int NS = DO_S ? T::KS * T::KB : 0;
-  constexpr int N = NO + NS;
-  constexpr int PF = 4;
-  static_assert(N >= PF, "pipeline depth");
+  static constexpr int NO = DO_O ? T::KB * 2 * T::MT : 0;
+  static constexpr int NS = DO_S ? T::KS * T::KB : 0;
+  static constexpr int N = NO + NS;
+  static_assert(N >= kPF, "pipeline depth");
+  // O op i: P block kb, 16-key half u, O^T row block mt (mt fastest).
+  __device__ static inline void o_op(int i, int& kb, int& u, int& mt) {
+    kb = i / (2 * T::MT);
+    u = (i / T::MT) % 2;
+    mt = i % T::MT;
+  }
+  // S op i: d step ks, key block kb (kb fastest).
+  __device__ static inline void s_op(int i, int& ks, int& kb) {
+    ks = i / T::KB;
+    kb = i % T::KB;
+  }
+  __device__ static inline u32x4 read(const char* __restrict__ vl, const char* __restrict__ kl, int t, int lane) {
+    if (t < NO) {
+      int kb, u, mt;
+      o_op(t, kb, u, mt);
+      return vt_operand<D, ROWS>(vl, mt, 2 * kb + u, lane);
+    }
+    int ks, kb;
+    s_op(t - NO, ks, kb);
+    return k_operand<D, ROWS>(kl, kb, ks, lane);
+  }
+};
+
+template <int D, int ROWS, bool DO_O, bool DO_S>
+__device__ inline void mma_prefetch(u32x4 (&buf)[kPF], const char* __restrict__ vl, const char* __restrict__ kl,
+                                    int lane) {
+#pragma unroll
+  for (int t = 0; t < kPF; ++t) buf[t] = MmaPlan<D, ROWS, DO_O, DO_S>::read(vl, kl, t, lane);
+}
+
+template <int DT, int D, int ROWS, bool DO_O, bool DO_S>
+__device__ inline void mma_run(u32x4 (&buf)[kPF], const char* __restrict__ vl, const char* __restrict__ kl,
+                               const uint32_t (&pk)[ROWS / 32][8], const u32x4 (&qop)[D / 16],
+                               f32x16 (&acc_o)[D / 32], f32x16 (&s)[ROWS / 32], int lane) {
+  using P = MmaPlan<D, ROWS, DO_O, DO_S>;
+  using T = Tile<D, ROWS>;
   if constexpr (DO_S) {
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
   }
-  auto rd = [&](int t) -> u32x4 {
-    if (t < NO) {
-      const int kb = t / (2 * T::MT), u = (t / T::MT) % 2, mt = t % T::MT;
-      return vt_operand<D, ROWS>(vl, mt, 2 * kb + u, lane);
-    }
-    const int t2 = t - NO, ks = t2 / T::KB, kb = t2 % T::KB;
-    return k_operand<D, ROWS>(kl, kb, ks, lane);
-  };
-  u32x4 buf[PF];
 #pragma unroll
-  for (int t = 0; t < PF; ++t) buf[t] = rd(t);
-#pragma unroll
-  for (int t = 0; t < N; ++t) {
-    const u32x4 a = buf[t % PF];
-    if (t + PF < N) buf[t % PF] = rd(t + PF);
-    if (t < NO) {
-      const int kb = t / (2 * T::MT), u = (t / T::MT) % 2, mt = t % T::MT;
+  for (int t = 0; t < P::N; ++t) {
+    const u32x4 a = buf[t % kPF];
+    if (t + kPF < P::N) buf[t % kPF] = P::read(vl, kl, t + kPF, lane);
+    if (t < P::NO) {
+      int kb, u, mt;
+      P::o_op(t, kb, u, mt);
       const u32x4 b = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
       acc_o[mt] = mfma32<DT>(a, b, acc_o[mt]);
     } else {
-      const int t2 = t - NO, ks = t2 / T::KB, kb = t2 % T::KB;
+      int ks, kb;
+      P::s_op(t - P::NO, ks, kb);
       s[kb] = mfma32<DT>(a, qop[ks], s[kb]);
     }
   }
-  // Keep the issue order: PF reads, then (MFMA, read) pairs, then the tail.
-  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+  // Keep the issue order: (MFMA, next read) pairs, then the tail MFMAs.
 #pragma unroll
-  for (int t = 0; t < N; ++t) {
+  for (int t = 0; t < P::N; ++t) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (t + PF < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (t + kPF < P::N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
 }
 
