@@ -3,15 +3,19 @@
 // Decode reads every cached K/V row once and does little arithmetic per byte,
 // so its time is set by memory traffic ("Advanced techniques for enhancing LLM
 // throughput", cabseo.com, "Autoregressive and memory-bound operations"). The
-// keys of each (sequence, kv-head) are cut into chunks; one workgroup streams
-// one chunk through LDS and serves all q-heads of the group from that single
-// read (grouped-query attention, SDPA page, devhandbook.co.kr, Example 5).
+// keys of each (sequence, kv-head) are cut into chunks; one wave streams one
+// chunk and serves all q-heads of the group from that single read
+// (grouped-query attention, SDPA page, devhandbook.co.kr, Example 5).
 //
-// Split kernel: workgroup (b, g, chunk s). Each tile of 128 keys is shared by
-// 4 waves, wave w taking keys [32w, 32w+32). The q-heads of group g are the
-// columns of the MFMA B operand (up to 32; unused columns are zero). Each wave
-// keeps its own running max/sum; the four are merged in LDS at the end and
-// the chunk's normalised output and LSE go to the workspace.
+// Split kernel: one wave per (b, g, chunk s), no workgroup barriers. Keys
+// move in blocks of 32. K goes from HBM straight into the A-operand registers
+// of S^T = K Q^T (lane l holds key l%32); V goes through a per-wave LDS tile
+// in row-major order and is read back transposed with ds_read_b64_tr_b16 as
+// the A operand of O^T += V^T P^T. The q-heads of group g are the columns of
+// the B operand (up to 32; unused columns are zero). The next block's loads
+// are issued as soon as the current block's registers are consumed, so each
+// wave keeps a block in flight while it computes. The chunk's normalised
+// output and LSE go to the workspace.
 // Combine kernel: per (b, h), merge the chunks of sequence b with the LSE form
 // of the softmax-merge identity ("The math of Flash Attention", unite.ai).
 #include "fa_launch.h"
@@ -21,125 +25,161 @@ namespace fa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kRows = 128;  // keys per tile
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kBlk = 32;  // keys per block
+
+// V block in LDS: row-major [32][D], 16-byte chunks XOR-swizzled by row so
+// that the 8 rows one transposed read touches fall in distinct banks.
+template <int D>
+struct VBlock {
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int RPB = 256 / (2 * D);   // rows per 256 bytes of banks
+  static constexpr int BYTES = kBlk * D * 2;
+  static constexpr int PER_LANE = kBlk * CPR / 64;  // chunks per lane
+  __device__ static inline int sw(int row) { return 4 * ((row / RPB) % (CPR / 4)); }
+  __device__ static inline int off(int row, int chunk) { return row * (2 * D) + ((chunk ^ sw(row)) * 16); }
+};
+
+// Transposed read of the A operand of O^T += V^T P^T for O^T rows 32*mt.. and
+// the 16-key group G of the block. ds_read_b64_tr_b16 gives lane i of each
+// 16-lane group element i%4 of lanes 4e + i/4 (e = 0..3); lane 4e+q therefore
+// points at key row 16G + 8p + 4h + e, columns 32mt + 16*dh + 4q .. +3, so lane
+// l ends up with V[16G + 8p + 4h + e][32mt + l%32] for e = 0..3, which is the
+// key order of the P accumulator (p = 0, 1 are the two halves).
+template <int D>
+__device__ inline u32x4 vt_tr_operand(const char* __restrict__ vl, int mt, int G, int lane) {
+  using V = VBlock<D>;
+  const int gi = lane >> 4, s = lane & 15, e = s >> 2, q = s & 3;
+  const int h = gi >> 1, dh = gi & 1;
+  const int chunk = 4 * mt + 2 * dh + (q >> 1);
+  u32x4 out;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int row = 16 * G + 8 * p + 4 * h + e;
+    const char* addr = vl + V::off(row, chunk) + 8 * (q & 1);
+    const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(addr));
+    const u32x2 w = __builtin_bit_cast(u32x2, t);
+    out[2 * p] = w[0];
+    out[2 * p + 1] = w[1];
+  }
+  return out;
+}
 
 template <int DT, int D>
-__global__ __launch_bounds__(kThreads, 1) void fa_decode_split_kernel(
+__global__ __launch_bounds__(64, 8) void fa_decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ seqlens, float* __restrict__ ws_o, float* __restrict__ ws_lse, int Hq, int Hkv,
     int Lcap, int chunk, int n_split, float scale_log2) {
-  using T = Tile<D, kRows>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::STAGE_BYTES];
+  constexpr int KS = D / 16, MT = D / 32, CPR = D / 8;
+  using V = VBlock<D>;
+  __shared__ __attribute__((aligned(16))) char vl[V::BYTES];
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int L = min(max(seqlens[b], 0), Lcap);
   const int k0 = s * chunk;
-  if (k0 >= L) return;  // whole workgroup: this chunk holds no cached rows
-  const int k1 = min(k0 + chunk, L);
+  if (k0 >= L) return;  // this chunk holds no cached rows
+  const int n = min(k0 + chunk, L) - k0;
   const int grp = Hq / Hkv;
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
+  const int lane = threadIdx.x, half = lane >> 5;
   const int col = lane & 31;  // q-head within the group (B-operand column)
   const size_t bg = (size_t)b * Hkv + g;
   const uint16_t* kp = kc + (bg * Lcap + k0) * D;
   const uint16_t* vp = vc + (bg * Lcap + k0) * D;
 
-  u32x4 qop[T::KS];
+  u32x4 qop[KS];
 #pragma unroll
-  for (int ks = 0; ks < T::KS; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     if (col < grp)
       qop[ks] = *reinterpret_cast<const u32x4*>(q + ((size_t)b * Hq + g * grp + col) * D + 16 * ks + 8 * half);
     else
       qop[ks] = u32x4{0u, 0u, 0u, 0u};
   }
 
-  f32x16 acc_o[T::MT];
+  f32x16 acc_o[MT];
 #pragma unroll
-  for (int mt = 0; mt < T::MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[mt][r] = 0.f;
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
-  const int n = k1 - k0;
-  const int n_t = (n + kRows - 1) / kRows;
-  TileRegs<D, kRows> regs;
-  load_tile<D, kRows>(kp, vp, min(kRows, n), regs);
-  store_tile<D, kRows>(smem, regs);
-  __syncthreads();
+  // Block loads. Rows at or beyond n re-read row n-1 (their scores are
+  // masked to -inf, so they contribute 0); no row past L is touched.
+  u32x4 ka[KS];         // K: lane holds key l%32, d chunk 2ks + l/32
+  u32x4 vr[V::PER_LANE];  // V: chunk lane + 64i of the row-major block
+  auto load_k = [&](int j0) {
+    const int row = min(j0 + col, n - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      ka[ks] = *reinterpret_cast<const u32x4*>(kp + (size_t)row * D + 16 * ks + 8 * half);
+  };
+  auto load_v = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < V::PER_LANE; ++i) {
+      const int ci = lane + 64 * i;
+      const int row = min(j0 + ci / CPR, n - 1);
+      vr[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)row * D + (ci % CPR) * 8);
+    }
+  };
+  load_k(0);
+  load_v(0);
 
-  for (int jt = 0; jt < n_t; ++jt) {
-    const int j0 = jt * kRows;
-    const bool more = jt + 1 < n_t;
-    if (more) {
-      const int jn = j0 + kRows;
-      load_tile<D, kRows>(kp + (size_t)jn * D, vp + (size_t)jn * D, min(kRows, n - jn), regs);
+  const int nb = (n + kBlk - 1) / kBlk;
+  for (int bi = 0; bi < nb; ++bi) {
+    const int j0 = bi * kBlk;
+    const bool more = bi + 1 < nb;
+    // ---- S^T = K Q^T for this block; then K registers are free for the next block
+    f32x16 sacc[1];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[0][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) sacc[0] = mfma32<DT>(ka[ks], qop[ks], sacc[0]);
+    if (more) load_k(j0 + kBlk);
+    // ---- V block to LDS (previous block's transposed reads are complete:
+    // every LDS read of this wave returned before its MFMA issued)
+#pragma unroll
+    for (int i = 0; i < V::PER_LANE; ++i) {
+      const int ci = lane + 64 * i;
+      *reinterpret_cast<u32x4*>(vl + V::off(ci / CPR, ci % CPR)) = vr[i];
     }
-    const char* st = smem + (jt & 1) * T::STAGE_BYTES;
-    const int jw = j0 + 32 * wave;  // first key of this wave's block (chunk-relative)
-    if (jw < n) {
-      f32x16 s_acc;
+    if (more) load_v(j0 + kBlk);
+    // ---- mask the ragged end of the chunk, online softmax
+    if (j0 + kBlk > n) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_acc[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < T::KS; ++ks) s_acc = mfma32<DT>(k_operand<D, kRows>(st, wave, ks, lane), qop[ks], s_acc);
-      if (jw + 32 > n) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (jw + acc_key(r, half) >= n) s_acc[r] = -__builtin_inff();
-      }
-      f32x16 s1[1] = {s_acc};
-      uint32_t pk1[1][8];
-      softmax_step<DT, 1, T::MT>(s1, scale_log2, m_run, l_run, acc_o, pk1);
-      const uint32_t* pk = pk1[0];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const u32x4 bop = {pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]};
-#pragma unroll
-        for (int mt = 0; mt < T::MT; ++mt)
-          acc_o[mt] = mfma32<DT>(vt_operand<D, kRows>(st + T::K_BYTES, mt, 2 * wave + u, lane), bop, acc_o[mt]);
-      }
+      for (int r = 0; r < 16; ++r)
+        if (j0 + acc_key(r, half) >= n) sacc[0][r] = -__builtin_inff();
     }
-    if (more) store_tile<D, kRows>(smem + ((jt + 1) & 1) * T::STAGE_BYTES, regs);
-    __syncthreads();
+    uint32_t pk[1][8];
+    softmax_step<DT, 1, MT>(sacc, scale_log2, m_run, l_run, acc_o, pk);
+    // ---- O^T += V^T P^T (LDS writes of this wave complete before its reads)
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the V block is in LDS
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const u32x4 bop = {pk[0][4 * u], pk[0][4 * u + 1], pk[0][4 * u + 2], pk[0][4 * u + 3]};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc_o[mt] = mfma32<DT>(vt_tr_operand<D>(vl, mt, u, lane), bop, acc_o[mt]);
+    }
   }
 
-  // ---- merge the 4 waves' partial states in LDS (stage buffers are free now)
+  // ---- chunk result: normalised O (fp32) and LSE to the workspace
   const float l_tot = halves_sum(l_run);
-  float* red_o = reinterpret_cast<float*>(smem);             // [4][grp][D]
-  float* red_m = red_o + 4 * 32 * D;                          // [4][32]
-  float* red_l = red_m + 4 * 32;                              // [4][32]
   if (col < grp) {
+    const size_t row = ((size_t)b * Hq + g * grp + col) * n_split + s;
+    const float inv = 1.f / l_tot;  // l_tot > 0: the chunk holds at least one key
+    float* orow = ws_o + row * D;
 #pragma unroll
-    for (int mt = 0; mt < T::MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = 32 * mt + acc_key(r, half);
-        red_o[(wave * 32 + col) * D + d] = acc_o[mt][r];
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * mt + 8 * i + 4 * half;
+        float4 w = {acc_o[mt][4 * i] * inv, acc_o[mt][4 * i + 1] * inv, acc_o[mt][4 * i + 2] * inv,
+                    acc_o[mt][4 * i + 3] * inv};
+        *reinterpret_cast<float4*>(orow + d0) = w;
       }
-    if (half == 0) {
-      red_m[wave * 32 + col] = m_run;
-      red_l[wave * 32 + col] = l_tot;
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < grp * D; idx += kThreads) {
-    const int c = idx / D, d = idx % D;
-    float mstar = -__builtin_inff();
-#pragma unroll
-    for (int w = 0; w < 4; ++w) mstar = fmaxf(mstar, red_m[w * 32 + c]);
-    float lsum = 0.f, osum = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = red_m[w * 32 + c];
-      const float f = (mw == -__builtin_inff()) ? 0.f : exp2_fast(mw - mstar);
-      lsum += f * red_l[w * 32 + c];
-      osum += f * red_o[(w * 32 + c) * D + d];
-    }
-    const size_t row = ((size_t)b * Hq + g * grp + c) * n_split + s;
-    ws_o[row * D + d] = osum / lsum;
-    if (d == 0) ws_lse[row] = (mstar + __builtin_log2f(lsum)) * kLn2;
+    if (half == 0) ws_lse[row] = (m_run + __builtin_log2f(l_tot)) * kLn2;
   }
 }
 
@@ -185,7 +225,7 @@ template <int DT, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   float* ws_o = reinterpret_cast<float*>(a.workspace);
   float* ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + a.ws_lse_offset);
-  hipLaunchKernelGGL((fa_decode_split_kernel<DT, D>), dim3(a.n_split, a.Hkv, a.B), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((fa_decode_split_kernel<DT, D>), dim3(a.n_split, a.Hkv, a.B), dim3(64), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.seqlens, ws_o,
                      ws_lse, a.Hq, a.Hkv, a.Lcap, a.chunk, a.n_split, a.scale * kLog2e);
   hipError_t e = hipGetLastError();
