@@ -184,41 +184,69 @@ __global__ __launch_bounds__(64, 8) void fa_decode_split_kernel(
 }
 
 // Merge the chunk results of (b, h): LSE = log sum_s exp(LSE_s),
-// O = sum_s exp(LSE_s - LSE) O_s. One workgroup of 64 threads per (b, h).
+// O = sum_s exp(LSE_s - LSE) O_s. One wave per (b, h): the lanes reduce the
+// chunk LSEs together, then each lane accumulates D/64 output elements over
+// the chunks, eight row loads in flight at a time.
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
 template <int DT, int D>
 __global__ __launch_bounds__(64) void fa_decode_combine_kernel(const float* __restrict__ ws_o,
                                                                const float* __restrict__ ws_lse,
                                                                const int32_t* __restrict__ seqlens,
                                                                uint16_t* __restrict__ o, float* __restrict__ lse,
                                                                int Hq, int Lcap, int chunk, int n_split) {
+  constexpr int PER = D / 64;
   const int bh = blockIdx.x;
   const int b = bh / Hq;
+  const int lane = threadIdx.x;
   const int L = min(max(seqlens[b], 0), Lcap);
   const int ns = (L + chunk - 1) / chunk;
   const float* lp = ws_lse + (size_t)bh * n_split;
-  const float* op = ws_o + (size_t)bh * n_split * D;
-  float mstar = -__builtin_inff();
-  for (int s = 0; s < ns; ++s) mstar = fmaxf(mstar, lp[s]);
+  const float* op = ws_o + (size_t)bh * n_split * D + lane * PER;
+  float m = -__builtin_inff();
+  for (int s = lane; s < ns; s += 64) m = fmaxf(m, lp[s]);
+  m = wave_max(m);
   float sum = 0.f;
-  for (int s = 0; s < ns; ++s) sum += __expf(lp[s] - mstar);
-  const float lse_all = (ns > 0) ? mstar + __logf(sum) : -__builtin_inff();
-  constexpr int PER = D / 64;
+  for (int s = lane; s < ns; s += 64) sum += __expf(lp[s] - m);
+  sum = wave_sum(sum);
+  const float lse_all = (ns > 0) ? m + __logf(sum) : -__builtin_inff();
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float wgt = __expf(lp[s] - lse_all);
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const float w = (s0 + lane < ns) ? __expf(lp[s0 + lane] - lse_all) : 0.f;
+    const int cnt = min(64, ns - s0);
+    for (int j = 0; j < cnt; j += 8) {
+      float rows[8][PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += wgt * op[(size_t)s * D + threadIdx.x * PER + i];
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) rows[u][i] = (j + u < cnt) ? op[(size_t)(s0 + j + u) * D + i] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j + u));
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] += wj * rows[u][i];
+      }
+    }
   }
   uint16_t* orow = o + (size_t)bh * D;
   if constexpr (PER == 2) {
-    *reinterpret_cast<uint32_t*>(orow + threadIdx.x * 2) = pack2<DT>(acc[0], acc[1]);
+    *reinterpret_cast<uint32_t*>(orow + lane * 2) = pack2<DT>(acc[0], acc[1]);
   } else {
     const uint32_t w = pack2<DT>(acc[0], 0.f);
-    orow[threadIdx.x] = (uint16_t)(w & 0xFFFFu);
+    orow[lane] = (uint16_t)(w & 0xFFFFu);
   }
-  if (lse != nullptr && threadIdx.x == 0) lse[bh] = lse_all;
+  if (lse != nullptr && lane == 0) lse[bh] = lse_all;
 }
 
 template <int DT, int D>
