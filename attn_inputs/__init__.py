@@ -38,12 +38,12 @@ FP16_NAN_BITS = 0x7E00
 
 # The five workloads: shapes, dtype, mask. Seed of config k is k.
 CONFIGS = {
-    "c1_tiny_mha": dict(seed=1, B=1, Hq=8, Hkv=8, N=128, d=64, dtype=BF16, causal=(False,)),
-    "c2_mid_mha": dict(seed=2, B=2, Hq=8, Hkv=8, N=4096, d=64, dtype=FP16, causal=(False, True)),
-    "c3_llama3_8b_gqa": dict(seed=3, B=1, Hq=32, Hkv=8, N=8192, d=128, dtype=BF16, causal=(True,)),
-    "c4_long_context": dict(seed=4, B=1, Hq=32, Hkv=8, N=131072, d=128, dtype=BF16, causal=(True,),
+    "tiny_mha_n128": dict(seed=1, B=1, Hq=8, Hkv=8, N=128, d=64, dtype=BF16, causal=(False,)),
+    "mha_n4096_fp16": dict(seed=2, B=2, Hq=8, Hkv=8, N=4096, d=64, dtype=FP16, causal=(False, True)),
+    "llama3_8b_gqa_n8192": dict(seed=3, B=1, Hq=32, Hkv=8, N=8192, d=128, dtype=BF16, causal=(True,)),
+    "llama3_8b_gqa_n131072": dict(seed=4, B=1, Hq=32, Hkv=8, N=131072, d=128, dtype=BF16, causal=(True,),
                             sample_rows=256),
-    "c5_decode": dict(seed=5, B=32, Hq=32, Hkv=8, Lcap=32768, d=128, dtype=BF16,
+    "decode_32seq_gqa": dict(seed=5, B=32, Hq=32, Hkv=8, Lcap=32768, d=128, dtype=BF16,
                       len_lo=1024, len_hi=32768),
 }
 

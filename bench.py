@@ -19,9 +19,9 @@ sample of the same workload on the host cores.
 
 Other modes (used to take rocprofv3 counter readings):
   --calibrate-copy   time a plain device copy of known size (counter scale)
-  --config NAME      a single configuration (c1_tiny_mha, c2_mid_mha,
-                     c2_mid_mha_causal, c3_llama3_8b_gqa, c4_long_context,
-                     c5_decode)
+  --config NAME      a single configuration (tiny_mha_n128, mha_n4096_fp16,
+                     mha_n4096_fp16_causal, llama3_8b_gqa_n8192, llama3_8b_gqa_n131072,
+                     decode_32seq_gqa)
 """
 from __future__ import annotations
 
@@ -126,7 +126,7 @@ class Prefill:
 
 
 class Decode:
-    def __init__(self, fa, name="c5_decode", num_splits=0):
+    def __init__(self, fa, name="decode_32seq_gqa", num_splits=0):
         import torch
         c = ai.CONFIGS[name]
         self.fa = fa
@@ -189,7 +189,7 @@ def cpu_cores_used():
     return cores
 
 
-def cpu_baseline_prefill(name="c3_llama3_8b_gqa", heads=8):
+def cpu_baseline_prefill(name="llama3_8b_gqa_n8192", heads=8):
     """The oracle on `heads` full heads of the prefill workload (all query rows,
     all keys, causal): TFLOP/s by the same FLOP convention as the GPU."""
     import oracle
@@ -211,7 +211,7 @@ def cpu_baseline_prefill(name="c3_llama3_8b_gqa", heads=8):
                       f"(float64 NumPy, score matrix materialised); {elapsed:.1f}s"}
 
 
-def cpu_baseline_decode(name="c5_decode", seqs=32):
+def cpu_baseline_decode(name="decode_32seq_gqa", seqs=32):
     import oracle
     c = ai.CONFIGS[name]
     lens = ai.decode_lengths(c["seed"], c["B"], c["len_lo"], c["len_hi"])[:seqs]
@@ -272,12 +272,12 @@ def main():
     fa.load_library()
 
     cfg = args.config
-    run_prefill = cfg in ("default", "c1_tiny_mha", "c2_mid_mha", "c2_mid_mha_causal", "c3_llama3_8b_gqa", "c4_long_context")
-    run_decode = cfg in ("default", "c5_decode")
+    run_prefill = cfg in ("default", "tiny_mha_n128", "mha_n4096_fp16", "mha_n4096_fp16_causal", "llama3_8b_gqa_n8192", "llama3_8b_gqa_n131072")
+    run_decode = cfg in ("default", "decode_32seq_gqa")
     if not (run_prefill or run_decode):
         raise SystemExit(f"unknown --config {cfg}")
-    pname = "c3_llama3_8b_gqa" if cfg == "default" else cfg.replace("_causal", "")
-    causal = cfg in ("default", "c3_llama3_8b_gqa", "c4_long_context", "c2_mid_mha_causal")
+    pname = "llama3_8b_gqa_n8192" if cfg == "default" else cfg.replace("_causal", "")
+    causal = cfg in ("default", "llama3_8b_gqa_n8192", "llama3_8b_gqa_n131072", "mha_n4096_fp16_causal")
     parts = []
     pre = dec = None
     if run_prefill:
@@ -307,22 +307,22 @@ def main():
         t_ms = float(np.mean(per[i]))
         gbs = dec.bytes / (t_ms * 1e-3) / 1e9
         droof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic("fa_decode_c5_counters.md"),
+                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic("fa_decode_32seq_gqa_counters.md"),
                  "algorithmic_bytes": dec.bytes}
-        out["decode"] = {"workload": "c5_decode", "ms_mean": round(t_ms, 4), "ms_min": round(float(np.min(per[i])), 4),
+        out["decode"] = {"workload": "decode_32seq_gqa", "ms_mean": round(t_ms, 4), "ms_min": round(float(np.min(per[i])), 4),
                          "value": round(gbs, 1), "unit": "GB/s", "roofline": droof}
         if pre is None:
             out.update(value=round(gbs, 1), unit="GB/s", roofline=droof)
     out.update({
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if cfg != "c2_mid_mha" and cfg != "c2_mid_mha_causal" else "fp16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if cfg != "mha_n4096_fp16" and cfg != "mha_n4096_fp16_causal" else "fp16",
         "data": "synthetic: seeded N(0,1) rounded to bf16/fp16",
-        "config": {"workload": "c3 prefill (B=1,Hq=32,Hkv=8,N=8192,d=128,causal) + c5 decode (32 seq, Hq=32,Hkv=8,d=128, L~U[1024,32768])"
+        "config": {"workload": "llama3_8b_gqa_n8192 prefill (B=1,Hq=32,Hkv=8,N=8192,d=128,causal,bf16) + decode_32seq_gqa (32 seq x 1 token, Hq=32,Hkv=8,d=128,bf16, L~U[1024,32768])"
                    if cfg == "default" else cfg,
                    "kernel_source_sha256": kernel_source_hash()},
     })
     if not args.no_cpu_baseline:
-        if pre is not None and pname == "c3_llama3_8b_gqa":
+        if pre is not None and pname == "llama3_8b_gqa_n8192":
             out["cpu_baseline"] = cpu_baseline_prefill()
             if dec is not None:
                 out["decode"]["cpu_baseline"] = cpu_baseline_decode()

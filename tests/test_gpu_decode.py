@@ -43,8 +43,8 @@ def decode_case(fa, seed, B, Hq, Hkv, Lcap, d, dt, lens, num_splits=0):
     return x, o, lse, m
 
 
-def test_c5_decode_full(fa):
-    c = ai.CONFIGS["c5_decode"]
+def test_decode_32seq_gqa_full(fa):
+    c = ai.CONFIGS["decode_32seq_gqa"]
     lens = ai.decode_lengths(c["seed"], c["B"], c["len_lo"], c["len_hi"])
     decode_case(fa, c["seed"], c["B"], c["Hq"], c["Hkv"], c["Lcap"], c["d"], c["dtype"], lens)
 

@@ -30,8 +30,8 @@ def full_case(fa, seed, B, Hq, Hkv, Nq, Nk, d, dtype, causal):
                    f"B{B} Hq{Hq} Hkv{Hkv} Nq{Nq} Nk{Nk} d{d} {dtype} causal={causal}")
 
 
-def test_c1_tiny_mha(fa):
-    c = ai.CONFIGS["c1_tiny_mha"]
+def test_tiny_mha_n128(fa):
+    c = ai.CONFIGS["tiny_mha_n128"]
     full_case(fa, c["seed"], c["B"], c["Hq"], c["Hkv"], c["N"], c["N"], c["d"], c["dtype"], False)
 
 
@@ -86,17 +86,17 @@ def sampled_case(fa, name, causal, rows_per_head):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_c2_mid_mha_sampled(fa, causal):
-    sampled_case(fa, "c2_mid_mha", causal, 128)
+def test_mha_n4096_fp16_sampled(fa, causal):
+    sampled_case(fa, "mha_n4096_fp16", causal, 128)
 
 
-def test_c3_llama3_gqa_sampled(fa):
-    sampled_case(fa, "c3_llama3_8b_gqa", True, 64)
+def test_llama3_gqa_n8192_sampled(fa):
+    sampled_case(fa, "llama3_8b_gqa_n8192", True, 64)
 
 
 @pytest.mark.slow
-def test_c4_long_context_sampled(fa):
-    sampled_case(fa, "c4_long_context", True, ai.CONFIGS["c4_long_context"]["sample_rows"])
+def test_llama3_8b_gqa_n131072_sampled(fa):
+    sampled_case(fa, "llama3_8b_gqa_n131072", True, ai.CONFIGS["llama3_8b_gqa_n131072"]["sample_rows"])
 
 
 # ---------------------------------------------------------------- GPU-side pins
@@ -154,7 +154,7 @@ def test_gqa_equals_repeated_mha_bitwise(fa):
 def test_deterministic_bitwise(fa):
     import torch
     announce("fwd determinism")
-    c = ai.CONFIGS["c3_llama3_8b_gqa"]
+    c = ai.CONFIGS["llama3_8b_gqa_n8192"]
     x = ai.prefill_inputs(c["seed"], 1, 32, 8, 2048, 128, ai.BF16)
     o1, l1 = run_fwd(fa, x, True)
     o2, l2 = run_fwd(fa, x, True)

@@ -74,7 +74,7 @@ def test_generator_hashes():
         assert digest(*args) == want[name], name
 
 
-def test_c5_lengths_in_range():
-    cfg = ai.CONFIGS["c5_decode"]
+def test_decode_lengths_in_range():
+    cfg = ai.CONFIGS["decode_32seq_gqa"]
     lens = ai.decode_lengths(cfg["seed"], cfg["B"], cfg["len_lo"], cfg["len_hi"])
     assert lens.min() >= 1024 and lens.max() <= 32768 and len(lens) == 32
