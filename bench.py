@@ -46,7 +46,7 @@ MFMA_PEAK_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 40
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "exact_tiled_attention_fwd_amd", "csrc", f)
-                  for f in ("fa_tile.h", "fa_fwd.hip", "fa_decode.hip", "fa_launch.h", "fa_api.cpp")]
+                  for f in ("fa_tile.h", "fa_fwd.hip", "fa_fwd_d128.hip", "fa_decode.hip", "fa_launch.h", "fa_api.cpp")]
 
 
 def log(*a):

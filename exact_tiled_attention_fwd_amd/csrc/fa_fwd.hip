@@ -27,42 +27,6 @@ namespace {
 constexpr int kBM = kFwdBlockRows;  // query rows per workgroup
 constexpr int kThreads = 512;  // 8 waves = 2 groups of 4
 
-// Work item of a workgroup: (b, kv-head g, q-head h, query tile qt).
-struct Work {
-  int b, g, h, qt;
-};
-
-// Heavy query tiles first (causal: later tiles see more keys), and when the
-// (batch, kv-head) pairs divide evenly over the 8 XCDs, each XCD's share of
-// workgroup ids maps to a fixed set of kv-heads so their K/V stay in that
-// XCD's L2. Workgroup id L runs on XCD L % 8.
-__device__ inline Work map_work(int L, int B, int Hq, int Hkv, int n_qt) {
-  const int grp = Hq / Hkv;
-  const int nbg = B * Hkv;
-  int qt, bg, hh;
-  if ((nbg & 7) == 0) {
-    const int x = L & 7, s = L >> 3;
-    const int nbx = nbg >> 3;
-    const int per = nbx * grp;
-    qt = n_qt - 1 - s / per;
-    const int r = s % per;
-    bg = x * nbx + r / grp;
-    hh = r % grp;
-  } else {
-    const int per = nbg * grp;
-    qt = n_qt - 1 - L / per;
-    const int r = L % per;
-    bg = r / grp;
-    hh = r % grp;
-  }
-  Work w;
-  w.b = bg / Hkv;
-  w.g = bg % Hkv;
-  w.h = w.g * grp + hh;
-  w.qt = qt;
-  return w;
-}
-
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -235,6 +199,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
+  if (a.d == 128) return launch_fwd_d128(a, stream);
   const bool c = a.causal != 0;
   if (a.dtype == DT_BF16) {
     if (a.d == 128) return c ? launch_fwd_t<DT_BF16, 128, true>(a, stream) : launch_fwd_t<DT_BF16, 128, false>(a, stream);

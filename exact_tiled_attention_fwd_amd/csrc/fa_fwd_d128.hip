@@ -1,0 +1,305 @@
+// fa_fwd_d128.hip - prefill attention forward for gfx950, head width 128.
+//
+// Same work split and schedule as the general kernel: one workgroup owns 256
+// query rows of one (batch, q-head), 8 waves of 32 rows in two groups of 4
+// that alternate between matrix-core phases and online-softmax phases, Q-outer
+// and K/V-inner ("Implementation details", "Flash Attention: Revolutionizing
+// Transformer Efficiency", unite.ai; the merge identity of "The math of Flash
+// Attention" on the same page).
+//
+// What differs is how K and V reach LDS. Every wave moves its share of each
+// tile HBM -> LDS directly (global_load_lds_dwordx4: no staging registers, no
+// LDS store instructions, no vector-ALU work), into 3-slot rings issued two
+// tiles (K) and one tile (V) ahead of the step that reads them. V stays
+// row-major in LDS and is read transposed (ds_read_b64_tr_b16) as the A
+// operand of O^T += V^T P^T, so no lane shuffles are needed anywhere. The
+// vector ALUs are left to the softmax.
+#include "fa_launch.h"
+#include "fa_tile.h"
+
+namespace fa {
+
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kBM = kFwdBlockRows;  // 256 query rows per workgroup
+constexpr int kThreads = 512;       // 8 waves = 2 groups of 4
+constexpr int kD = 128;
+constexpr int kRows = 64;           // keys per tile
+constexpr int kSlots = 3;           // ring depth for K and for V
+constexpr int kTile = kRows * kD * 2;  // 16 KiB
+constexpr int KS = kD / 16;         // 8 MFMA k-steps over d
+constexpr int KB = kRows / 32;      // 2 key blocks of 32
+constexpr int MT = kD / 32;         // 4 row blocks of O^T
+
+// LDS layouts, row-major [64][128] 16-bit = 16 chunks of 16 bytes per row:
+//   K: chunk c of row r at position c ^ (r % 16): the 32 rows of an A-operand
+//      fetch of one chunk column land on distinct banks;
+//   V: chunk c of row r at position c ^ 4 (r % 4): conflict-free transposed
+//      reads (each 16-lane group reads 4 rows x 32 bytes).
+__device__ inline int k_phys(int row, int c) { return c ^ (row & 15); }
+__device__ inline int v_phys(int row, int c) { return c ^ (4 * (row & 3)); }
+
+// Byte offset in the global tile of the 16-byte chunk that DMA instruction i
+// of wave w writes to LDS position p = 512 i + 64 w + lane (row p / 16,
+// position p % 16). The swizzles are involutions, so position -> chunk uses
+// the same map. Rows at or beyond nvalid re-read row nvalid - 1: their scores
+// are masked to -inf and contribute exactly 0.
+template <bool IS_V>
+__device__ inline uint32_t dma_src(int i, int wave, int lane, int nvalid) {
+  const int p = 512 * i + 64 * wave + lane;
+  const int row = p >> 4, pos = p & 15;
+  const int c = IS_V ? v_phys(row, pos) : k_phys(row, pos);
+  return (uint32_t)(min(row, nvalid - 1) * (kD * 2) + c * 16);
+}
+
+// One 1 KiB direct-to-LDS load: lane l's 16 bytes from sbase + voff land at
+// LDS address lds + 16 l. Written as asm so that the compiler's wait
+// insertion, which cannot tell the ring slots apart, does not wait for every
+// load in flight before each LDS read; the phase barriers do the waiting.
+__device__ __attribute__((always_inline)) inline void dma16(const uint16_t* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// Barrier that first waits until this thread has at most `pending` (0, 2 or
+// 4, wave-uniform) direct-to-LDS loads outstanding. No release fence: it
+// would also wait for the loads that are meant to stay in flight.
+__device__ __attribute__((always_inline)) inline void dma_barrier(int pending) {
+  if (pending >= 4)
+    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+  else if (pending >= 2)
+    __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2)
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+__device__ __attribute__((always_inline)) inline void plain_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Operand reader of the layouts above. K: one 16-byte read per lane (row
+// 32 kb + lane % 32, chunk 2 ks + lane / 32). V^T: two transposed reads; lane
+// l gets V[16 G + 8 p + 4 h + e][32 mt + l % 32] for e = 0..3, p = 0, 1
+// (h = l / 32), which is the key order of the P accumulator.
+struct DmaReader {
+  static constexpr int VT_READS = 2;
+  __device__ static inline u32x4 k(const char* __restrict__ kl, int kb, int ks, int lane) {
+    const int row = 32 * kb + (lane & 31);
+    return *reinterpret_cast<const u32x4*>(kl + row * 256 + k_phys(row, 2 * ks + (lane >> 5)) * 16);
+  }
+  __device__ static inline u32x4 vt(const char* __restrict__ vl, int mt, int G, int lane) {
+    const int gi = lane >> 4, e = (lane >> 2) & 3, qq = lane & 3;
+    const int h = gi >> 1, dh = gi & 1;
+    const int c = 4 * mt + 2 * dh + (qq >> 1);
+    u32x4 out;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int row = 16 * G + 8 * p + 4 * h + e;
+      const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(vl + row * 256 + v_phys(row, c) * 16 + 8 * (qq & 1)));
+      const u32x2 w = __builtin_bit_cast(u32x2, t);
+      out[2 * p] = w[0];
+      out[2 * p + 1] = w[1];
+    }
+    return out;
+  }
+};
+
+template <int DT, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void fa_fwd_d128_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Nq, int Nk,
+    float scale_log2, int n_qt) {
+  constexpr int D = kD, ROWS = kRows;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kSlots * kTile];
+  char* const kring = smem;                   // K tile t in slot t % 3
+  char* const vring = smem + kSlots * kTile;  // V tile t in slot t % 3
+
+  const Work wk = map_work(blockIdx.x, B, Hq, Hkv, n_qt);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int grp = wave >> 2;  // 0: matrix cores first; 1: softmax first
+  const int q0 = wk.qt * kBM;
+  const int q0w = q0 + 32 * wave;  // first query row of this wave
+  const int off = Nk - Nq;         // causal: key j visible to query i iff j <= i + off
+
+  const size_t bh = (size_t)wk.b * Hq + wk.h;
+  const size_t bg = (size_t)wk.b * Hkv + wk.g;
+  const uint16_t* qp = q + bh * Nq * D;
+  const uint16_t* kp = k + bg * Nk * D;
+  const uint16_t* vp = v + bg * Nk * D;
+
+  // Key tiles this workgroup visits.
+  int n_kv = (Nk + ROWS - 1) / ROWS;
+  if (CAUSAL) {
+    const int last_key = min(q0 + kBM, Nq) - 1 + off;
+    n_kv = min(n_kv, last_key / ROWS + 1);
+  }
+  // Key tiles this wave computes on (0 if the wave has no valid query row).
+  const bool wave_active = q0w < Nq;
+  int wave_tiles = wave_active ? n_kv : 0;
+  if (CAUSAL && wave_active) wave_tiles = min(n_kv, (min(q0w + 31, Nq - 1) + off) / ROWS + 1);
+
+  // Q^T operand (B operand of S^T = K Q^T), held for the whole loop.
+  const int qrow = q0w + (lane & 31);
+  u32x4 qop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    if (qrow < Nq)
+      qop[ks] = *reinterpret_cast<const u32x4*>(qp + (size_t)qrow * D + 16 * ks + 8 * half);
+    else
+      qop[ks] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // Wait for Q here, once: the tile loads are asm the compiler does not count,
+  // so a Q wait it placed inside the loop would also wait for them.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+  f32x16 acc_o[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[mt][r] = 0.f;
+  float m_run = -__builtin_inff();  // row reference point, log2 units
+  float l_run = 0.f;                // this lane's share of the running sum
+  f32x16 s[KB];                     // S^T of the tile last multiplied
+  uint32_t pk[KB][8];               // P of the tile last softmaxed
+
+  // SM(j): mask the ragged key tail / causal diagonal, online softmax -> pk.
+  auto softmax = [&](int j) {
+    const int j0 = j * ROWS;
+    const bool need_mask = (j0 + ROWS > Nk) || (CAUSAL && j0 + ROWS - 1 > q0w + off);
+    if (need_mask) {
+      const int lim = CAUSAL ? min(Nk, qrow + off + 1) : Nk;  // keys < lim are visible
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (j0 + 32 * kb + acc_key(r, half) >= lim) s[kb][r] = -__builtin_inff();
+    }
+    softmax_step<DT, KB, MT>(s, scale_log2, m_run, l_run, acc_o, pk);
+  };
+  // Matrix-core phase: MB(jo) = O^T += V^T_jo P^T (if do_o), MA(js) = S^T = K_js Q^T (if do_s).
+  // mma_pre issues the first operand reads; mma finishes the phase.
+  u32x4 obuf[kPF];
+  auto mma_pre = [&](bool do_o, int jo, bool do_s, int js) {
+    const char* vl = vring + (jo % kSlots) * kTile;
+    const char* kl = kring + (js % kSlots) * kTile;
+    if (do_o && do_s)
+      mma_prefetch<D, ROWS, true, true, DmaReader>(obuf, vl, kl, lane);
+    else if (do_o)
+      mma_prefetch<D, ROWS, true, false, DmaReader>(obuf, vl, kl, lane);
+    else if (do_s)
+      mma_prefetch<D, ROWS, false, true, DmaReader>(obuf, vl, kl, lane);
+  };
+  auto mma = [&](bool do_o, int jo, bool do_s, int js) {
+    const char* vl = vring + (jo % kSlots) * kTile;
+    const char* kl = kring + (js % kSlots) * kTile;
+    if (do_o && do_s)
+      mma_run<DT, D, ROWS, true, true, DmaReader>(obuf, vl, kl, pk, qop, acc_o, s, lane);
+    else if (do_o)
+      mma_run<DT, D, ROWS, true, false, DmaReader>(obuf, vl, kl, pk, qop, acc_o, s, lane);
+    else if (do_s)
+      mma_run<DT, D, ROWS, false, true, DmaReader>(obuf, vl, kl, pk, qop, acc_o, s, lane);
+  };
+
+  // ---- direct-to-LDS tile loads: 2 instructions per wave per tile
+  const uint32_t lds_k = (uint32_t)(uintptr_t)(lds_void_t*)kring;
+  const uint32_t lds_v = (uint32_t)(uintptr_t)(lds_void_t*)vring;
+  auto issue = [&](bool is_v, int t) {
+    const int nvalid = min(ROWS, Nk - t * ROWS);
+    const uint16_t* base = (is_v ? vp : kp) + (size_t)t * ROWS * D;
+    const uint32_t slot = (is_v ? lds_v : lds_k) + (uint32_t)((t % kSlots) * kTile) + (uint32_t)(64 * wv * 16);
+    const uint32_t s0 = is_v ? dma_src<true>(0, wv, lane, nvalid) : dma_src<false>(0, wv, lane, nvalid);
+    const uint32_t s1 = is_v ? dma_src<true>(1, wv, lane, nvalid) : dma_src<false>(1, wv, lane, nvalid);
+    dma16(base, s0, slot);
+    dma16(base, s1, slot + 512 * 16);
+  };
+  // Loads issued at the start of step i: K_{i+2} and V_{i+1}; returns the
+  // number of load instructions (wave-uniform).
+  auto issue_step = [&](int i) -> int {
+    int n = 0;
+    if (i + 2 < n_kv) {
+      issue(false, i + 2);
+      n += 2;
+    }
+    if (i + 1 < n_kv) {
+      issue(true, i + 1);
+      n += 2;
+    }
+    return n;
+  };
+
+  // Prologue: K_0 (read first), then K_1 and V_0 (the loads of "step -1").
+  if (0 < n_kv) issue(false, 0);
+  dma_barrier(issue_step(-1));  // K_0 has landed
+
+  // Macro-step i = phase A, barrier Y_i, phase B, barrier X_{i+1}:
+  //   group 0: A = MB(i-1), MA(i)                          B = SM(i), first reads of MB(i), MA(i+1)
+  //   group 1: A = SM(i-1), first reads of MB(i-1), MA(i)  B = MB(i-1), MA(i)
+  // Step i reads K_i and V_{i-1}, and after Y_i also K_{i+1} and V_i. The
+  // loads issued at the start of step i (K_{i+2}, V_{i+1}) go to the slots of
+  // K_{i-1} and V_{i-2}, last read in step i - 1; Y_i waits for the loads
+  // issued at step i - 1 (K_{i+1}, V_i).
+  if (grp == 0) {
+    mma_pre(false, 0, 0 < wave_tiles, 0);
+    for (int i = 0; i <= n_kv; ++i) {
+      const int n_new = issue_step(i);
+      mma(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
+      dma_barrier(n_new);  // Y_i
+      if (i < wave_tiles) softmax(i);
+      mma_pre(i < wave_tiles, i, i + 1 < wave_tiles, i + 1);
+      plain_barrier();  // X_{i+1}
+    }
+  } else {
+    for (int i = 0; i <= n_kv; ++i) {
+      const int n_new = issue_step(i);
+      if (i >= 1 && i - 1 < wave_tiles) softmax(i - 1);
+      mma_pre(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
+      dma_barrier(n_new);  // Y_i
+      mma(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
+      plain_barrier();  // X_{i+1}
+    }
+  }
+
+  if (!wave_active) return;
+  // ---- epilogue: normalise once, write O and LSE
+  const float l_tot = halves_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < Nq) {
+    uint16_t* orow = o + bh * Nq * D + (size_t)qrow * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * mt + 8 * i + 4 * half;
+        const u32x2 w = {pack2<DT>(acc_o[mt][4 * i] * inv, acc_o[mt][4 * i + 1] * inv),
+                         pack2<DT>(acc_o[mt][4 * i + 2] * inv, acc_o[mt][4 * i + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + d0) = w;
+      }
+    if (lse != nullptr && half == 0)
+      lse[bh * Nq + qrow] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
+  }
+}
+
+template <int DT, bool CAUSAL>
+hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
+  const int n_qt = (a.Nq + kBM - 1) / kBM;
+  const long long nblocks = (long long)n_qt * a.B * a.Hq;
+  if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fa_fwd_d128_kernel<DT, CAUSAL>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
+                     a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_qt);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_d128(const FwdArgs& a, hipStream_t stream) {
+  const bool c = a.causal != 0;
+  if (a.dtype == DT_BF16) return c ? launch_t<DT_BF16, true>(a, stream) : launch_t<DT_BF16, false>(a, stream);
+  return c ? launch_t<DT_FP16, true>(a, stream) : launch_t<DT_FP16, false>(a, stream);
+}
+
+}  // namespace fa

@@ -233,7 +233,20 @@ __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 // are already complete), mma_run does the rest.
 constexpr int kPF = 4;
 
-template <int D, int ROWS, bool DO_O, bool DO_S>
+// Operand reader of the register-staged layouts above (K swizzled, V stored
+// transposed): one LDS read per operand.
+template <int D, int ROWS>
+struct StagedReader {
+  static constexpr int VT_READS = 1;  // LDS read instructions per V^T operand
+  __device__ static inline u32x4 k(const char* __restrict__ kl, int kb, int ks, int lane) {
+    return k_operand<D, ROWS>(kl, kb, ks, lane);
+  }
+  __device__ static inline u32x4 vt(const char* __restrict__ vl, int mt, int G, int lane) {
+    return vt_operand<D, ROWS>(vl, mt, G, lane);
+  }
+};
+
+template <int D, int ROWS, bool DO_O, bool DO_S, class RD = StagedReader<D, ROWS>>
 struct MmaPlan {
   using T = Tile<D, ROWS>;
   static constexpr int NO = DO_O ? T::KB * 2 * T::MT : 0;
@@ -255,26 +268,26 @@ struct MmaPlan {
     if (t < NO) {
       int kb, u, mt;
       o_op(t, kb, u, mt);
-      return vt_operand<D, ROWS>(vl, mt, 2 * kb + u, lane);
+      return RD::vt(vl, mt, 2 * kb + u, lane);
     }
     int ks, kb;
     s_op(t - NO, ks, kb);
-    return k_operand<D, ROWS>(kl, kb, ks, lane);
+    return RD::k(kl, kb, ks, lane);
   }
 };
 
-template <int D, int ROWS, bool DO_O, bool DO_S>
+template <int D, int ROWS, bool DO_O, bool DO_S, class RD = StagedReader<D, ROWS>>
 __device__ inline void mma_prefetch(u32x4 (&buf)[kPF], const char* __restrict__ vl, const char* __restrict__ kl,
                                     int lane) {
 #pragma unroll
-  for (int t = 0; t < kPF; ++t) buf[t] = MmaPlan<D, ROWS, DO_O, DO_S>::read(vl, kl, t, lane);
+  for (int t = 0; t < kPF; ++t) buf[t] = MmaPlan<D, ROWS, DO_O, DO_S, RD>::read(vl, kl, t, lane);
 }
 
-template <int DT, int D, int ROWS, bool DO_O, bool DO_S>
+template <int DT, int D, int ROWS, bool DO_O, bool DO_S, class RD = StagedReader<D, ROWS>>
 __device__ inline void mma_run(u32x4 (&buf)[kPF], const char* __restrict__ vl, const char* __restrict__ kl,
                                const uint32_t (&pk)[ROWS / 32][8], const u32x4 (&qop)[D / 16],
                                f32x16 (&acc_o)[D / 32], f32x16 (&s)[ROWS / 32], int lane) {
-  using P = MmaPlan<D, ROWS, DO_O, DO_S>;
+  using P = MmaPlan<D, ROWS, DO_O, DO_S, RD>;
   using T = Tile<D, ROWS>;
   if constexpr (DO_S) {
 #pragma unroll
@@ -297,11 +310,13 @@ __device__ inline void mma_run(u32x4 (&buf)[kPF], const char* __restrict__ vl, c
       s[kb] = mfma32<DT>(a, qop[ks], s[kb]);
     }
   }
-  // Keep the issue order: (MFMA, next read) pairs, then the tail MFMAs.
+  // Keep the issue order: (MFMA, next operand's reads) pairs, then the tail
+  // MFMAs.
 #pragma unroll
   for (int t = 0; t < P::N; ++t) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (t + kPF < P::N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (t + kPF < P::NO) __builtin_amdgcn_sched_group_barrier(0x100, RD::VT_READS, 0);
+    else if (t + kPF < P::N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
 }
 
@@ -319,23 +334,73 @@ __device__ inline float halves_sum(float x) {
 // Key offset (within a 32-key block) of accumulator register r in lane half h.
 __device__ inline int acc_key(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// Rescale threshold, log2 units. The reference point m of a row (the value
-// subtracted before exponentiating) only moves up when a tile's maximum
-// exceeds it by more than this; exp(m_old - m_new) is then applied to the
-// running sum and the output accumulator. Any reference point gives the same
-// exact result (the merge identity of "The math of Flash Attention",
-// unite.ai, holds for any common shift); this one keeps every p <= 2^8 and
-// lets most tiles skip the rescale.
-constexpr float kRescaleLog2 = 8.f;
+// Reference-point rule of the online softmax. Any common shift m gives the
+// same exact result (the merge identity of "The math of Flash Attention",
+// unite.ai, holds for any shift), so m only has to keep the exponentials in
+// range. A tile is first exponentiated against the current m with no
+// maximum taken; only when some lane's sum of those exponentials leaves
+// (0, kSumLimit] (or m is still -inf: the row's first tile) is the tile's row
+// maximum taken, m moved to it, the running sum and the output accumulator
+// rescaled by exp(m_old - m_new), and the tile exponentiated again. Every p
+// is at most kSumLimit, so nothing overflows, and bf16 P keeps its relative
+// precision at any magnitude.
+constexpr float kSumLimit = 65536.f;
+constexpr float kRescaleLog2 = 8.f;  // threshold of the max-first form below
 
 // One online-softmax step over NS 32-key blocks of S^T (raw scores, masked
 // entries -inf). c = scale*log2(e). Updates the row reference m_run (log2
 // units, per lane = per query column), this lane's share of the running sum
 // l_run, rescales acc_o when m_run moves, and returns P rounded to the input
 // type, packed two per register in accumulator order.
+template <int DT, int NS>
+__device__ __attribute__((always_inline)) inline float exp_tile(const f32x16 (&s)[NS], float c, float m_use, uint32_t (&pk)[NS][8]) {
+  float psum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < NS; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = exp2_fast(__builtin_fmaf(s[kb][r], c, -m_use));
+      const float p1 = exp2_fast(__builtin_fmaf(s[kb][r + 1], c, -m_use));
+      psum += p0 + p1;
+      pk[kb][r >> 1] = pack2<DT>(p0, p1);
+    }
+  return psum;
+}
+
 template <int DT, int NS, int MT>
-__device__ inline void softmax_step(f32x16 (&s)[NS], float c, float& m_run, float& l_run, f32x16 (&acc_o)[MT],
+__device__ __attribute__((always_inline)) inline void softmax_step(f32x16 (&s)[NS], float c, float& m_run, float& l_run, f32x16 (&acc_o)[MT],
                                     uint32_t (&pk)[NS][8]) {
+  float psum = 0.f;
+  bool slow = __builtin_amdgcn_ballot_w64(m_run == -__builtin_inff()) != 0;
+  if (!slow) {
+    psum = exp_tile<DT, NS>(s, c, m_run, pk);
+    slow = __builtin_amdgcn_ballot_w64(!(psum <= kSumLimit)) != 0;
+  }
+  if (slow) {
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < NS; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = halves_max(mx) * c;
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_new == -__builtin_inff()) ? 1.f : exp2_fast(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
+    m_run = m_new;
+    psum = exp_tile<DT, NS>(s, c, (m_new == -__builtin_inff()) ? 0.f : m_new, pk);
+  }
+  l_run += psum;
+}
+
+// Max-first form of the step (the row maximum of every tile is taken; m
+// moves only when it exceeds m by more than kRescaleLog2).
+template <int DT, int NS, int MT>
+__device__ __attribute__((always_inline)) inline void softmax_step_maxfirst(f32x16 (&s)[NS], float c, float& m_run, float& l_run,
+                                             f32x16 (&acc_o)[MT], uint32_t (&pk)[NS][8]) {
   float mx = -__builtin_inff();
 #pragma unroll
   for (int kb = 0; kb < NS; ++kb)
@@ -352,18 +417,44 @@ __device__ inline void softmax_step(f32x16 (&s)[NS], float c, float& m_run, floa
       for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
     m_run = m_new;
   }
-  const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
-  float psum = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < NS; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = exp2_fast(__builtin_fmaf(s[kb][r], c, -m_use));
-      const float p1 = exp2_fast(__builtin_fmaf(s[kb][r + 1], c, -m_use));
-      psum += p0 + p1;
-      pk[kb][r >> 1] = pack2<DT>(p0, p1);
-    }
-  l_run += psum;
+  l_run += exp_tile<DT, NS>(s, c, (m_run == -__builtin_inff()) ? 0.f : m_run, pk);
+}
+
+// ------------------------------------------------------------------ work order
+// Work item of a workgroup: (b, kv-head g, q-head h, query tile qt).
+struct Work {
+  int b, g, h, qt;
+};
+
+// Heavy query tiles first (causal: later tiles see more keys), and when the
+// (batch, kv-head) pairs divide evenly over the 8 XCDs, each XCD's share of
+// workgroup ids maps to a fixed set of kv-heads so their K/V stay in that
+// XCD's L2. Workgroup id L runs on XCD L % 8.
+__device__ inline Work map_work(int L, int B, int Hq, int Hkv, int n_qt) {
+  const int grp = Hq / Hkv;
+  const int nbg = B * Hkv;
+  int qt, bg, hh;
+  if ((nbg & 7) == 0) {
+    const int x = L & 7, s = L >> 3;
+    const int nbx = nbg >> 3;
+    const int per = nbx * grp;
+    qt = n_qt - 1 - s / per;
+    const int r = s % per;
+    bg = x * nbx + r / grp;
+    hh = r % grp;
+  } else {
+    const int per = nbg * grp;
+    qt = n_qt - 1 - L / per;
+    const int r = L % per;
+    bg = r / grp;
+    hh = r % grp;
+  }
+  Work w;
+  w.b = bg / Hkv;
+  w.g = bg % Hkv;
+  w.h = w.g * grp + hh;
+  w.qt = qt;
+  return w;
 }
 
 }  // namespace fa
