@@ -7,7 +7,7 @@
 // Transformer Efficiency", unite.ai; the merge identity of "The math of Flash
 // Attention" on the same page).
 //
-// What differs is how K and V reach LDS. Every wave moves its share of each
+// What differs is how K and V reach LDS. The waves of one group move each
 // tile HBM -> LDS directly (global_load_lds_dwordx4: no staging registers, no
 // LDS store instructions, no vector-ALU work), into 3-slot rings issued two
 // tiles (K) and one tile (V) ahead of the step that reads them. V stays
@@ -43,14 +43,17 @@ constexpr int MT = kD / 32;         // 4 row blocks of O^T
 __device__ inline int k_phys(int row, int c) { return c ^ (row & 15); }
 __device__ inline int v_phys(int row, int c) { return c ^ (4 * (row & 3)); }
 
-// Byte offset in the global tile of the 16-byte chunk that DMA instruction i
-// of wave w writes to LDS position p = 512 i + 64 w + lane (row p / 16,
-// position p % 16). The swizzles are involutions, so position -> chunk uses
-// the same map. Rows at or beyond nvalid re-read row nvalid - 1: their scores
-// are masked to -inf and contribute exactly 0.
+// Byte offset in the global tile of the 16-byte chunk that load instruction
+// i (0..3) of wave w (0..3 of the loading group) writes to LDS position
+// p = 256 i + 64 w + lane (row p / 16, position p % 16). The swizzles are
+// involutions, so position -> chunk uses the same map. Rows at or beyond
+// nvalid re-read row nvalid - 1: their scores are masked to -inf and
+// contribute exactly 0. For a full tile the offset of instruction i is that
+// of instruction 0 plus 4096 i (the swizzles depend on the row only through
+// row % 16), so one offset register serves all four.
 template <bool IS_V>
-__device__ inline uint32_t dma_src(int i, int wave, int lane, int nvalid) {
-  const int p = 512 * i + 64 * wave + lane;
+__device__ inline uint32_t dma_src(int i, int w, int lane, int nvalid) {
+  const int p = 256 * i + 64 * w + lane;
   const int row = p >> 4, pos = p & 15;
   const int c = IS_V ? v_phys(row, pos) : k_phys(row, pos);
   return (uint32_t)(min(row, nvalid - 1) * (kD * 2) + c * 16);
@@ -65,14 +68,14 @@ __device__ __attribute__((always_inline)) inline void dma16(const uint16_t* sbas
                : "memory", "m0");
 }
 
-// Barrier that first waits until this thread has at most `pending` (0, 2 or
-// 4, wave-uniform) direct-to-LDS loads outstanding. No release fence: it
+// Barrier that first waits until this thread has at most `pending` (0, 4 or
+// 8, wave-uniform) direct-to-LDS loads outstanding. No release fence: it
 // would also wait for the loads that are meant to stay in flight.
 __device__ __attribute__((always_inline)) inline void dma_barrier(int pending) {
-  if (pending >= 4)
+  if (pending >= 8)
+    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+  else if (pending >= 4)
     __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
-  else if (pending >= 2)
-    __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2)
   else
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   asm volatile("s_barrier" ::: "memory");
@@ -85,6 +88,7 @@ __device__ __attribute__((always_inline)) inline void plain_barrier() { asm vola
 // (h = l / 32), which is the key order of the P accumulator.
 struct DmaReader {
   static constexpr int VT_READS = 2;
+  static constexpr bool INTERLEAVE = true;  // transposed reads are slower per wave: spread them
   __device__ static inline u32x4 k(const char* __restrict__ kl, int kb, int ks, int lane) {
     const int row = 32 * kb + (lane & 31);
     return *reinterpret_cast<const u32x4*>(kl + row * 256 + k_phys(row, 2 * ks + (lane >> 5)) * 16);
@@ -104,6 +108,26 @@ struct DmaReader {
       out[2 * p + 1] = w[1];
     }
     return out;
+  }
+};
+
+// The 8 tile loads of one step, slotted in after MFMAs 2, 6, ..., 30 of a
+// 32-op matrix-core phase, so that the loads of the four loading waves reach
+// the address unit a few at a time instead of in one burst. Full tiles only.
+struct DmaSpread {
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  uint32_t kslot, vslot;
+  bool has_k, has_v;
+  uint32_t dk, dv;
+  __device__ __attribute__((always_inline)) void operator()(int t) const {
+    if ((t & 3) != 2) return;
+    const int j = t >> 2;
+    if (j < 4) {
+      if (has_k) dma16(kbase + 2048 * j, dk, kslot + 4096 * j);
+    } else {
+      if (has_v) dma16(vbase + 2048 * (j - 4), dv, vslot + 4096 * (j - 4));
+    }
   }
 };
 
@@ -204,35 +228,45 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_d128_kernel(
       mma_run<DT, D, ROWS, false, true, DmaReader>(obuf, vl, kl, pk, qop, acc_o, s, lane);
   };
 
-  // ---- direct-to-LDS tile loads: 2 instructions per wave per tile
+  // ---- direct-to-LDS tile loads, issued by the waves of group 0 only (they
+  // wait at the Y barrier anyway): 4 instructions per wave per tile.
   const uint32_t lds_k = (uint32_t)(uintptr_t)(lds_void_t*)kring;
   const uint32_t lds_v = (uint32_t)(uintptr_t)(lds_void_t*)vring;
+  const int wg = wv & 3;  // wave index within its group
+  const uint32_t dk = dma_src<false>(0, wg, lane, ROWS);  // source offsets of a full tile
+  const uint32_t dv = dma_src<true>(0, wg, lane, ROWS);
   auto issue = [&](bool is_v, int t) {
     const int nvalid = min(ROWS, Nk - t * ROWS);
     const uint16_t* base = (is_v ? vp : kp) + (size_t)t * ROWS * D;
-    const uint32_t slot = (is_v ? lds_v : lds_k) + (uint32_t)((t % kSlots) * kTile) + (uint32_t)(64 * wv * 16);
-    const uint32_t s0 = is_v ? dma_src<true>(0, wv, lane, nvalid) : dma_src<false>(0, wv, lane, nvalid);
-    const uint32_t s1 = is_v ? dma_src<true>(1, wv, lane, nvalid) : dma_src<false>(1, wv, lane, nvalid);
-    dma16(base, s0, slot);
-    dma16(base, s1, slot + 512 * 16);
+    const uint32_t slot = (is_v ? lds_v : lds_k) + (uint32_t)((t % kSlots) * kTile) + (uint32_t)(64 * wg * 16);
+    if (nvalid == ROWS) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma16(base + 2048 * i, is_v ? dv : dk, slot + 4096 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dma16(base, is_v ? dma_src<true>(i, wg, lane, nvalid) : dma_src<false>(i, wg, lane, nvalid), slot + 4096 * i);
+    }
   };
   // Loads issued at the start of step i: K_{i+2} and V_{i+1}; returns the
-  // number of load instructions (wave-uniform).
+  // number of load instructions this thread issued (wave-uniform).
   auto issue_step = [&](int i) -> int {
     int n = 0;
-    if (i + 2 < n_kv) {
-      issue(false, i + 2);
-      n += 2;
-    }
-    if (i + 1 < n_kv) {
-      issue(true, i + 1);
-      n += 2;
+    if (grp == 0) {
+      if (i + 2 < n_kv) {
+        issue(false, i + 2);
+        n += 4;
+      }
+      if (i + 1 < n_kv) {
+        issue(true, i + 1);
+        n += 4;
+      }
     }
     return n;
   };
 
   // Prologue: K_0 (read first), then K_1 and V_0 (the loads of "step -1").
-  if (0 < n_kv) issue(false, 0);
+  if (grp == 0 && 0 < n_kv) issue(false, 0);
   dma_barrier(issue_step(-1));  // K_0 has landed
 
   // Macro-step i = phase A, barrier Y_i, phase B, barrier X_{i+1}:
@@ -245,8 +279,28 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_d128_kernel(
   if (grp == 0) {
     mma_pre(false, 0, 0 < wave_tiles, 0);
     for (int i = 0; i <= n_kv; ++i) {
-      const int n_new = issue_step(i);
-      mma(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
+      const bool do_o = i >= 1 && i - 1 < wave_tiles, do_s = i < wave_tiles;
+      const bool has_k = i + 2 < n_kv, has_v = i + 1 < n_kv;
+      const int n_new = 4 * has_k + 4 * has_v;
+      if (do_o && do_s) {
+        // full phase: with full tiles the loads are spread over its MFMAs
+        const bool spread = (!has_k || Nk - (i + 2) * ROWS >= ROWS) && (!has_v || Nk - (i + 1) * ROWS >= ROWS);
+        if (!spread) issue_step(i);
+        const DmaSpread ex{kp + (size_t)(i + 2) * ROWS * D, vp + (size_t)(i + 1) * ROWS * D,
+                           lds_k + (uint32_t)(((i + 2) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
+                           lds_v + (uint32_t)(((i + 1) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
+                           has_k && spread, has_v && spread, dk, dv};
+        mma_run<DT, D, ROWS, true, true, DmaReader>(obuf, vring + ((i - 1) % kSlots) * kTile,
+                                                    kring + (i % kSlots) * kTile, pk, qop, acc_o, s, lane, ex);
+      } else {
+        issue_step(i);
+        if (do_o)
+          mma_run<DT, D, ROWS, true, false, DmaReader>(obuf, vring + ((i - 1) % kSlots) * kTile,
+                                                       kring + (i % kSlots) * kTile, pk, qop, acc_o, s, lane);
+        else if (do_s)
+          mma_run<DT, D, ROWS, false, true, DmaReader>(obuf, vring, kring + (i % kSlots) * kTile, pk, qop, acc_o,
+                                                       s, lane);
+      }
       dma_barrier(n_new);  // Y_i
       if (i < wave_tiles) softmax(i);
       mma_pre(i < wave_tiles, i, i + 1 < wave_tiles, i + 1);

@@ -238,6 +238,7 @@ constexpr int kPF = 4;
 template <int D, int ROWS>
 struct StagedReader {
   static constexpr int VT_READS = 1;  // LDS read instructions per V^T operand
+  static constexpr bool INTERLEAVE = false;
   __device__ static inline u32x4 k(const char* __restrict__ kl, int kb, int ks, int lane) {
     return k_operand<D, ROWS>(kl, kb, ks, lane);
   }
@@ -253,6 +254,12 @@ struct MmaPlan {
   static constexpr int NS = DO_S ? T::KS * T::KB : 0;
   static constexpr int N = NO + NS;
   static_assert(N >= kPF, "pipeline depth");
+  // With both products in the phase and a reader that asks for it, O and S
+  // ops alternate (spreading the reads of the slower operand); otherwise the
+  // O ops come first.
+  static constexpr bool ALT = RD::INTERLEAVE && DO_O && DO_S && NO == NS;
+  __device__ static constexpr bool is_o(int t) { return ALT ? (t & 1) == 0 : t < NO; }
+  __device__ static constexpr int idx(int t) { return ALT ? t >> 1 : (t < NO ? t : t - NO); }
   // O op i: P block kb, 16-key half u, O^T row block mt (mt fastest).
   __device__ static inline void o_op(int i, int& kb, int& u, int& mt) {
     kb = i / (2 * T::MT);
@@ -265,28 +272,35 @@ struct MmaPlan {
     kb = i % T::KB;
   }
   __device__ static inline u32x4 read(const char* __restrict__ vl, const char* __restrict__ kl, int t, int lane) {
-    if (t < NO) {
+    if (is_o(t)) {
       int kb, u, mt;
-      o_op(t, kb, u, mt);
+      o_op(idx(t), kb, u, mt);
       return RD::vt(vl, mt, 2 * kb + u, lane);
     }
     int ks, kb;
-    s_op(t - NO, ks, kb);
+    s_op(idx(t), ks, kb);
     return RD::k(kl, kb, ks, lane);
   }
 };
 
 template <int D, int ROWS, bool DO_O, bool DO_S, class RD = StagedReader<D, ROWS>>
-__device__ inline void mma_prefetch(u32x4 (&buf)[kPF], const char* __restrict__ vl, const char* __restrict__ kl,
+__device__ __attribute__((always_inline)) inline void mma_prefetch(u32x4 (&buf)[kPF], const char* __restrict__ vl, const char* __restrict__ kl,
                                     int lane) {
 #pragma unroll
   for (int t = 0; t < kPF; ++t) buf[t] = MmaPlan<D, ROWS, DO_O, DO_S, RD>::read(vl, kl, t, lane);
 }
 
-template <int DT, int D, int ROWS, bool DO_O, bool DO_S, class RD = StagedReader<D, ROWS>>
-__device__ inline void mma_run(u32x4 (&buf)[kPF], const char* __restrict__ vl, const char* __restrict__ kl,
+// Work slotted in after each MFMA of a phase (called with the op index), or
+// between the exponentials of a softmax step; all() does all of it at once.
+struct NoExtra {
+  __device__ void operator()(int) const {}
+  __device__ void all() const {}
+};
+
+template <int DT, int D, int ROWS, bool DO_O, bool DO_S, class RD = StagedReader<D, ROWS>, class EX = NoExtra>
+__device__ __attribute__((always_inline)) inline void mma_run(u32x4 (&buf)[kPF], const char* __restrict__ vl, const char* __restrict__ kl,
                                const uint32_t (&pk)[ROWS / 32][8], const u32x4 (&qop)[D / 16],
-                               f32x16 (&acc_o)[D / 32], f32x16 (&s)[ROWS / 32], int lane) {
+                               f32x16 (&acc_o)[D / 32], f32x16 (&s)[ROWS / 32], int lane, const EX& ex = EX{}) {
   using P = MmaPlan<D, ROWS, DO_O, DO_S, RD>;
   using T = Tile<D, ROWS>;
   if constexpr (DO_S) {
@@ -299,24 +313,29 @@ __device__ inline void mma_run(u32x4 (&buf)[kPF], const char* __restrict__ vl, c
   for (int t = 0; t < P::N; ++t) {
     const u32x4 a = buf[t % kPF];
     if (t + kPF < P::N) buf[t % kPF] = P::read(vl, kl, t + kPF, lane);
-    if (t < P::NO) {
+    if (P::is_o(t)) {
       int kb, u, mt;
-      P::o_op(t, kb, u, mt);
+      P::o_op(P::idx(t), kb, u, mt);
       const u32x4 b = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
       acc_o[mt] = mfma32<DT>(a, b, acc_o[mt]);
     } else {
       int ks, kb;
-      P::s_op(t - P::NO, ks, kb);
+      P::s_op(P::idx(t), ks, kb);
       s[kb] = mfma32<DT>(a, qop[ks], s[kb]);
     }
+    ex(t);
   }
   // Keep the issue order: (MFMA, next operand's reads) pairs, then the tail
   // MFMAs.
 #pragma unroll
   for (int t = 0; t < P::N; ++t) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (t + kPF < P::NO) __builtin_amdgcn_sched_group_barrier(0x100, RD::VT_READS, 0);
-    else if (t + kPF < P::N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (t + kPF < P::N) {
+      if (P::is_o(t + kPF))
+        __builtin_amdgcn_sched_group_barrier(0x100, RD::VT_READS, 0);
+      else
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
   }
 }
 
@@ -345,15 +364,15 @@ __device__ inline int acc_key(int r, int h) { return 8 * (r >> 2) + 4 * h + (r &
 // is at most kSumLimit, so nothing overflows, and bf16 P keeps its relative
 // precision at any magnitude.
 constexpr float kSumLimit = 65536.f;
-constexpr float kRescaleLog2 = 8.f;  // threshold of the max-first form below
 
 // One online-softmax step over NS 32-key blocks of S^T (raw scores, masked
 // entries -inf). c = scale*log2(e). Updates the row reference m_run (log2
 // units, per lane = per query column), this lane's share of the running sum
 // l_run, rescales acc_o when m_run moves, and returns P rounded to the input
 // type, packed two per register in accumulator order.
-template <int DT, int NS>
-__device__ __attribute__((always_inline)) inline float exp_tile(const f32x16 (&s)[NS], float c, float m_use, uint32_t (&pk)[NS][8]) {
+template <int DT, int NS, class EX = NoExtra>
+__device__ __attribute__((always_inline)) inline float exp_tile(const f32x16 (&s)[NS], float c, float m_use,
+                                                                 uint32_t (&pk)[NS][8], const EX& ex = EX{}) {
   float psum = 0.f;
 #pragma unroll
   for (int kb = 0; kb < NS; ++kb)
@@ -363,17 +382,24 @@ __device__ __attribute__((always_inline)) inline float exp_tile(const f32x16 (&s
       const float p1 = exp2_fast(__builtin_fmaf(s[kb][r + 1], c, -m_use));
       psum += p0 + p1;
       pk[kb][r >> 1] = pack2<DT>(p0, p1);
+      ex(8 * kb + (r >> 1));
     }
   return psum;
 }
 
-template <int DT, int NS, int MT>
-__device__ __attribute__((always_inline)) inline void softmax_step(f32x16 (&s)[NS], float c, float& m_run, float& l_run, f32x16 (&acc_o)[MT],
-                                    uint32_t (&pk)[NS][8]) {
+// ex(i) is called once per pair of exponentials (i = 0 .. 8 NS - 1) of the
+// pass against the current reference point; a row's first tile, which has
+// no such pass, calls ex.all() instead.
+template <int DT, int NS, int MT, class EX = NoExtra>
+__device__ __attribute__((always_inline)) inline void softmax_step(f32x16 (&s)[NS], float c, float& m_run,
+                                                                   float& l_run, f32x16 (&acc_o)[MT],
+                                                                   uint32_t (&pk)[NS][8], const EX& ex = EX{}) {
   float psum = 0.f;
   bool slow = __builtin_amdgcn_ballot_w64(m_run == -__builtin_inff()) != 0;
-  if (!slow) {
-    psum = exp_tile<DT, NS>(s, c, m_run, pk);
+  if (slow) {
+    ex.all();
+  } else {
+    psum = exp_tile<DT, NS>(s, c, m_run, pk, ex);
     slow = __builtin_amdgcn_ballot_w64(!(psum <= kSumLimit)) != 0;
   }
   if (slow) {
@@ -394,30 +420,6 @@ __device__ __attribute__((always_inline)) inline void softmax_step(f32x16 (&s)[N
     psum = exp_tile<DT, NS>(s, c, (m_new == -__builtin_inff()) ? 0.f : m_new, pk);
   }
   l_run += psum;
-}
-
-// Max-first form of the step (the row maximum of every tile is taken; m
-// moves only when it exceeds m by more than kRescaleLog2).
-template <int DT, int NS, int MT>
-__device__ __attribute__((always_inline)) inline void softmax_step_maxfirst(f32x16 (&s)[NS], float c, float& m_run, float& l_run,
-                                             f32x16 (&acc_o)[MT], uint32_t (&pk)[NS][8]) {
-  float mx = -__builtin_inff();
-#pragma unroll
-  for (int kb = 0; kb < NS; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = halves_max(mx) * c;
-  if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0) {
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_new == -__builtin_inff()) ? 1.f : exp2_fast(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
-    m_run = m_new;
-  }
-  l_run += exp_tile<DT, NS>(s, c, (m_run == -__builtin_inff()) ? 0.f : m_run, pk);
 }
 
 // ------------------------------------------------------------------ work order
