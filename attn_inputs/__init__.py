@@ -27,7 +27,7 @@ import numpy as np
 __all__ = [
     "BF16", "FP16", "Q_ID", "K_ID", "V_ID",
     "round_to_bits", "bits_to_f64", "slab", "prefill_inputs",
-    "decode_lengths", "decode_inputs", "sample_rows", "CONFIGS",
+    "decode_lengths", "decode_inputs", "paged_layout", "sample_rows", "CONFIGS",
 ]
 
 BF16 = "bf16"
@@ -141,6 +141,33 @@ def decode_inputs(seed: int, B: int, Hq: int, Hkv: int, Lcap: int, d: int, dtype
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(job, work))
     return dict(q=q, k_cache=kc, v_cache=vc, seqlens=lengths, dtype=dtype)
+
+
+def paged_layout(k_cache: np.ndarray, v_cache: np.ndarray, page_size: int, seed: int, dtype: str,
+                 spare_pages: int = 0) -> dict:
+    """Scatter contiguous caches [B,Hkv,Lcap,d] into pages [num_pages,Hkv,page_size,d].
+
+    Page j of sequence b (rows j*page_size ..) goes to page id
+    block_table[b, j], taken from a seeded permutation
+    (``default_rng([seed, 6])``) of all num_pages = B*max_pages + spare_pages
+    ids; spare pages hold NaN bits. Pure data movement: the logical cache of
+    every sequence is unchanged.
+    """
+    B, Hkv, Lcap, d = k_cache.shape
+    assert Lcap % page_size == 0
+    max_pages = Lcap // page_size
+    num_pages = B * max_pages + spare_pages
+    perm = np.random.default_rng([seed, 6]).permutation(num_pages).astype(np.int32)
+    table = perm[: B * max_pages].reshape(B, max_pages)
+    nan_bits = BF16_NAN_BITS if dtype == BF16 else FP16_NAN_BITS
+    out = {}
+    for name, cache in (("k_pages", k_cache), ("v_pages", v_cache)):
+        pages = np.full((num_pages, Hkv, page_size, d), nan_bits, np.uint16)
+        pages[table.reshape(-1)] = (cache.reshape(B, Hkv, max_pages, page_size, d)
+                                    .transpose(0, 2, 1, 3, 4).reshape(-1, Hkv, page_size, d))
+        out[name] = pages
+    out.update(block_table=table, page_size=page_size)
+    return out
 
 
 def sample_rows(seed: int, head: int, N: int, count: int = 256) -> np.ndarray:

@@ -21,7 +21,8 @@ Other modes (used to take rocprofv3 counter readings):
   --calibrate-copy   time a plain device copy of known size (counter scale)
   --config NAME      a single configuration (tiny_mha_n128, mha_n4096_fp16,
                      mha_n4096_fp16_causal, llama3_8b_gqa_n8192, llama3_8b_gqa_n131072,
-                     decode_32seq_gqa)
+                     decode_32seq_gqa, decode_32seq_gqa_paged: the same decode with
+                     the cache in 128-row pages in a shuffled page order)
 """
 from __future__ import annotations
 
@@ -154,6 +155,40 @@ class Decode:
                        workspace=self.ws, out=self.o, lse=self.lse)
 
 
+class DecodePaged(Decode):
+    """The 32-sequence decode with each cache scattered over 128-row pages in
+    a seeded shuffled order (the same logical caches and byte count)."""
+
+    def __init__(self, fa, name="decode_32seq_gqa", num_splits=0, page_size=128):
+        import torch
+        c = ai.CONFIGS[name]
+        self.fa = fa
+        self.B, self.Hq, self.Hkv, self.Lcap, self.d, self.dtype = c["B"], c["Hq"], c["Hkv"], c["Lcap"], c["d"], c["dtype"]
+        self.page_size = page_size
+        t0 = time.time()
+        self.lens = ai.decode_lengths(c["seed"], self.B, c["len_lo"], c["len_hi"])
+        x = ai.decode_inputs(c["seed"], self.B, self.Hq, self.Hkv, self.Lcap, self.d, self.dtype, self.lens)
+        self.q = to_dev(x["q"], self.dtype)
+        pl = ai.paged_layout(x["k_cache"], x["v_cache"], page_size, c["seed"], self.dtype)
+        del x
+        self.kp = to_dev(pl["k_pages"], self.dtype)
+        self.vp = to_dev(pl["v_pages"], self.dtype)
+        self.table = torch.from_numpy(np.ascontiguousarray(pl["block_table"], np.int32)).cuda()
+        del pl
+        self.seqlens = torch.from_numpy(self.lens).cuda()
+        self.num_splits = num_splits
+        ws = fa.fa_decode_workspace_bytes(self.B, self.Hq, self.Hkv, self.Lcap, self.d, num_splits)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((self.B, self.Hq), dtype=torch.float32, device="cuda")
+        self.bytes = decode_bytes(self.lens, self.Hq, self.Hkv, self.d)
+        log(f"[bench] paged decode (page {page_size}): inputs ready in {time.time() - t0:.1f}s")
+
+    def __call__(self):
+        self.fa.decode_paged(self.q, self.kp, self.vp, self.table, self.seqlens, num_splits=self.num_splits,
+                             workspace=self.ws, out=self.o, lse=self.lse)
+
+
 def time_steps(parts, steps, warmup):
     """Warm up, then time exactly `steps` steps; per-part event timings."""
     import torch
@@ -211,7 +246,10 @@ def cpu_baseline_prefill(name="llama3_8b_gqa_n8192", heads=8):
                       f"(float64 NumPy, score matrix materialised); {elapsed:.1f}s"}
 
 
-def cpu_baseline_decode(name="decode_32seq_gqa", seqs=32):
+def cpu_baseline_decode(name="decode_32seq_gqa", seqs=32, page_size=0):
+    """The oracle's decode (paged decode when page_size > 0, through a
+    shuffled page table) on the first `seqs` sequences: GB/s by the same byte
+    count as the GPU."""
     import oracle
     c = ai.CONFIGS[name]
     lens = ai.decode_lengths(c["seed"], c["B"], c["len_lo"], c["len_hi"])[:seqs]
@@ -222,12 +260,26 @@ def cpu_baseline_decode(name="decode_32seq_gqa", seqs=32):
         q = np.stack([ai.bits_to_f64(ai.slab(c["seed"], ai.Q_ID, b, h, 1, d, dt), dt)[0] for h in range(Hq)])[None]
         kc = np.stack([ai.bits_to_f64(ai.slab(c["seed"], ai.K_ID, b, g, L, d, dt), dt) for g in range(Hkv)])[None]
         vc = np.stack([ai.bits_to_f64(ai.slab(c["seed"], ai.V_ID, b, g, L, d, dt), dt) for g in range(Hkv)])[None]
-        t0 = time.perf_counter()
-        oracle.decode(q, kc, vc, [L], 1.0 / math.sqrt(d))
+        if page_size:
+            n_pg = (L + page_size - 1) // page_size
+            pad = n_pg * page_size - L
+            kpad = np.concatenate([kc, np.zeros((1, Hkv, pad, d))], axis=2)
+            vpad = np.concatenate([vc, np.zeros((1, Hkv, pad, d))], axis=2)
+            order = np.random.default_rng([c["seed"], 7, b]).permutation(n_pg)
+            kp = np.empty((n_pg, Hkv, page_size, d))
+            vp = np.empty((n_pg, Hkv, page_size, d))
+            kp[order] = kpad[0].reshape(Hkv, n_pg, page_size, d).transpose(1, 0, 2, 3)
+            vp[order] = vpad[0].reshape(Hkv, n_pg, page_size, d).transpose(1, 0, 2, 3)
+            t0 = time.perf_counter()
+            oracle.decode_paged(q, kp, vp, order[None, :], [L], 1.0 / math.sqrt(d))
+        else:
+            t0 = time.perf_counter()
+            oracle.decode(q, kc, vc, [L], 1.0 / math.sqrt(d))
         elapsed += time.perf_counter() - t0
     nbytes = decode_bytes(lens, Hq, Hkv, d)
+    what = f"paged ({page_size}-row pages), " if page_size else ""
     return {"value": nbytes / elapsed / 1e9, "unit": "GB/s", "cores": cpu_cores_used(), "kind": "oracle",
-            "sample": f"first {seqs} of 32 sequences (lengths {lens.tolist()}), all 32 q-heads; {elapsed:.1f}s"}
+            "sample": f"{what}first {seqs} of 32 sequences (lengths {lens.tolist()}), all 32 q-heads; {elapsed:.1f}s"}
 
 
 # ------------------------------------------------------------------ modes
@@ -273,7 +325,8 @@ def main():
 
     cfg = args.config
     run_prefill = cfg in ("default", "tiny_mha_n128", "mha_n4096_fp16", "mha_n4096_fp16_causal", "llama3_8b_gqa_n8192", "llama3_8b_gqa_n131072")
-    run_decode = cfg in ("default", "decode_32seq_gqa")
+    run_decode = cfg in ("default", "decode_32seq_gqa", "decode_32seq_gqa_paged")
+    paged = cfg == "decode_32seq_gqa_paged"
     if not (run_prefill or run_decode):
         raise SystemExit(f"unknown --config {cfg}")
     pname = "llama3_8b_gqa_n8192" if cfg == "default" else cfg.replace("_causal", "")
@@ -284,7 +337,7 @@ def main():
         pre = Prefill(fa, pname, causal)
         parts.append(pre)
     if run_decode:
-        dec = Decode(fa, num_splits=args.num_splits)
+        dec = DecodePaged(fa, num_splits=args.num_splits) if paged else Decode(fa, num_splits=args.num_splits)
         parts.append(dec)
 
     wall, per = time_steps(parts, args.steps, args.warmup)
@@ -307,9 +360,9 @@ def main():
         t_ms = float(np.mean(per[i]))
         gbs = dec.bytes / (t_ms * 1e-3) / 1e9
         droof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic("fa_decode_32seq_gqa_counters.md"),
+                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic(f"fa_{cfg if paged else 'decode_32seq_gqa'}_counters.md"),
                  "algorithmic_bytes": dec.bytes}
-        out["decode"] = {"workload": "decode_32seq_gqa", "ms_mean": round(t_ms, 4), "ms_min": round(float(np.min(per[i])), 4),
+        out["decode"] = {"workload": cfg if paged else "decode_32seq_gqa", "ms_mean": round(t_ms, 4), "ms_min": round(float(np.min(per[i])), 4),
                          "value": round(gbs, 1), "unit": "GB/s", "roofline": droof}
         if pre is None:
             out.update(value=round(gbs, 1), unit="GB/s", roofline=droof)
@@ -327,7 +380,7 @@ def main():
             if dec is not None:
                 out["decode"]["cpu_baseline"] = cpu_baseline_decode()
         elif dec is not None:
-            out["cpu_baseline"] = cpu_baseline_decode()
+            out["cpu_baseline"] = cpu_baseline_decode(page_size=128 if paged else 0)
     print(json.dumps(out), flush=True)
 
 

@@ -6,11 +6,13 @@ runs in the HIP kernels of that library; this module only marshals arguments.
 PyTorch supplies device memory and the current stream.
 
 Raw entry points, same names and argument order as the C header:
-    fa_fwd, fa_decode, fa_decode_workspace_bytes, fa_status_string,
-    fa_last_error, fa_abi_version
+    fa_fwd, fa_decode, fa_decode_paged, fa_decode_workspace_bytes,
+    fa_status_string, fa_last_error, fa_abi_version
 Tensor-level helpers:
     attention(q, k, v, causal=False, scale=None) -> (o, lse)
     decode(q, k_cache, v_cache, seqlens, scale=None, num_splits=0) -> (o, lse)
+    decode_paged(q, k_pages, v_pages, block_table, seqlens, scale=None,
+                 num_splits=0) -> (o, lse)
 
 There is no fallback: if the library is missing or fails to load, every call
 raises.
@@ -26,8 +28,8 @@ import torch  # loads the HIP runtime that libfa.so then binds to
 __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
     "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FAError", "lib_path", "load_library",
-    "fa_fwd", "fa_decode", "fa_decode_workspace_bytes", "fa_status_string",
-    "fa_last_error", "fa_abi_version", "attention", "decode", "dtype_code",
+    "fa_fwd", "fa_decode", "fa_decode_paged", "fa_decode_workspace_bytes", "fa_status_string",
+    "fa_last_error", "fa_abi_version", "attention", "decode", "decode_paged", "dtype_code",
 ]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
@@ -73,6 +75,8 @@ def load_library():
     lib.fa_fwd.restype = i
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
     lib.fa_decode.restype = i
+    lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_decode_paged.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_status_string.argtypes = [i]
@@ -108,6 +112,14 @@ def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, workspace_bytes,
     """Call the C ``fa_decode`` with integer device addresses; returns the status."""
     return load_library().fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, workspace_bytes,
                                     B, Hq, Hkv, Lcap, d, scale, num_splits, dtype, stream)
+
+
+def fa_decode_paged(q, k_pages, v_pages, block_table, seqlens, o, lse, workspace, workspace_bytes,
+                    B, Hq, Hkv, num_pages, page_size, max_pages, d, scale, num_splits, dtype, stream) -> int:
+    """Call the C ``fa_decode_paged`` with integer device addresses; returns the status."""
+    return load_library().fa_decode_paged(q, k_pages, v_pages, block_table, seqlens, o, lse, workspace,
+                                          workspace_bytes, B, Hq, Hkv, num_pages, page_size, max_pages, d, scale,
+                                          num_splits, dtype, stream)
 
 
 def fa_decode_workspace_bytes(B, Hq, Hkv, Lcap, d, num_splits) -> int:
@@ -210,5 +222,42 @@ def decode(q, k_cache, v_cache, seqlens, scale: float | None = None, num_splits:
         st = fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(out), _ptr(lse),
                        _ptr(workspace), workspace.numel() * workspace.element_size(),
                        B, Hq, Hkv, Lcap, d, float(scale), int(num_splits), dtype_code(q.dtype), _stream(dev))
+    _raise_for(st)
+    return out, lse
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seqlens, scale: float | None = None, num_splits: int = 0,
+                 workspace=None, out=None, lse=None):
+    """Decode against a paged cache: q [B,Hq,d], pages [num_pages,Hkv,page_size,d],
+    block_table int32 [B,max_pages], seqlens int32 [B]."""
+    _check_tensor("q", q, 3)
+    dev = q.device
+    _check_tensor("k_pages", k_pages, 4, dev)
+    _check_tensor("v_pages", v_pages, 4, dev)
+    _check_tensor("block_table", block_table, 2, dev)
+    _check_tensor("seqlens", seqlens, 1, dev)
+    if seqlens.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "seqlens and block_table must be int32")
+    if k_pages.dtype != q.dtype or v_pages.dtype != q.dtype:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "q and the pages must share a dtype")
+    B, Hq, d = q.shape
+    num_pages, Hkv, page_size, dk = k_pages.shape
+    Bt, max_pages = block_table.shape
+    if dk != d or tuple(v_pages.shape) != tuple(k_pages.shape) or Bt != B or seqlens.shape[0] != B:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "shape mismatch between q, pages, block_table and seqlens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_decode_workspace_bytes(B, Hq, Hkv, max_pages * page_size, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        st = fa_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seqlens), _ptr(out),
+                             _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), B, Hq, Hkv,
+                             num_pages, page_size, max_pages, d, float(scale), int(num_splits), dtype_code(q.dtype),
+                             _stream(dev))
     _raise_for(st)
     return out, lse

@@ -155,6 +155,46 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Lcap, int d, int nu
   return make_plan(B, Hkv, Lcap, num_splits, Hq, d).ws_bytes;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared by fa_decode and fa_decode_paged: cache_elems is the element count
+// of each of k_cache / v_cache; table != nullptr selects the paged layout.
+fa_status decode_impl(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* table, const int32_t* seqlens, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, int B, int Hq, int Hkv, int Lcap, int d, float scale, int num_splits,
+                      int dtype, void* stream, size_t cache_bytes, int page_size, int max_pages, int num_pages) {
+  if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "%s: lse must be 4-byte aligned", fn);
+  if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "%s: num_splits must be >= 0", fn);
+  fa_status st = check_common(d, dtype, scale, Hq, Hkv);
+  if (st != FA_OK) return st;
+  if (Hq / Hkv > 32) return fail(FA_ERR_UNSUPPORTED, "at most 32 q-heads per kv-head (got %d)", Hq / Hkv);
+  if (B > 65535 || Hkv > 65535) return fail(FA_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
+  size_t qb;
+  if (!mul_bytes(qb, {B, Hq, d, 2})) return fail(FA_ERR_INVALID_ARG, "%s: tensor sizes overflow", fn);
+  const fa::DecodePlan p = make_plan(B, Hkv, Lcap, num_splits, Hq, d);
+  if (workspace_bytes < p.ws_bytes)
+    return fail(FA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, p.ws_bytes);
+  const size_t cb = cache_bytes;
+  if (overlap(o, qb, q, qb) || overlap(o, qb, k_cache, cb) || overlap(o, qb, v_cache, cb) ||
+      overlap(workspace, p.ws_bytes, q, qb) || overlap(workspace, p.ws_bytes, k_cache, cb) ||
+      overlap(workspace, p.ws_bytes, v_cache, cb) || overlap(workspace, p.ws_bytes, o, qb))
+    return fail(FA_ERR_INVALID_ARG, "o or workspace overlaps another tensor");
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::DecodeArgs a{q, k_cache, v_cache, seqlens, o, lse, workspace, p.ws_lse_offset, B, Hq, Hkv, Lcap, d, scale,
+                   p.chunk, p.n_split, dtype, table, page_size, max_pages, num_pages};
+  hipError_t e = fa::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens, void* o,
                     float* lse, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Lcap, int d,
                     float scale, int num_splits, int dtype, void* stream) {
@@ -164,32 +204,37 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, con
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16))
     return fail(FA_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
   if (!aligned(seqlens, 4)) return fail(FA_ERR_INVALID_ARG, "seqlens must be 4-byte aligned");
-  if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lcap <= 0 || d <= 0)
     return fail(FA_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d Lcap=%d d=%d)", B, Hq, Hkv, Lcap, d);
-  if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 0");
-  fa_status st = check_common(d, dtype, scale, Hq, Hkv);
-  if (st != FA_OK) return st;
-  if (Hq / Hkv > 32) return fail(FA_ERR_UNSUPPORTED, "at most 32 q-heads per kv-head (got %d)", Hq / Hkv);
-  if (B > 65535 || Hkv > 65535) return fail(FA_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
-  size_t qb, cb;
-  if (!mul_bytes(qb, {B, Hq, d, 2}) || !mul_bytes(cb, {B, Hkv, Lcap, d, 2}))
+  size_t cb;
+  if (!mul_bytes(cb, {B, Hkv, Lcap, d, 2})) return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
+  return decode_impl("fa_decode", q, k_cache, v_cache, nullptr, seqlens, o, lse, workspace, workspace_bytes, B, Hq,
+                     Hkv, Lcap, d, scale, num_splits, dtype, stream, cb, 0, 0, 0);
+}
+
+fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
+                          const int32_t* seqlens, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                          int B, int Hq, int Hkv, int num_pages, int page_size, int max_pages, int d, float scale,
+                          int num_splits, int dtype, void* stream) {
+  g_last_error.clear();
+  if (!q || !k_pages || !v_pages || !block_table || !seqlens || !o || !workspace)
+    return fail(FA_ERR_INVALID_ARG, "q, k_pages, v_pages, block_table, seqlens, o and workspace must be non-null");
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(o, 16))
+    return fail(FA_ERR_INVALID_ARG, "q, k_pages, v_pages and o must be 16-byte aligned");
+  if (!aligned(seqlens, 4) || !aligned(block_table, 4))
+    return fail(FA_ERR_INVALID_ARG, "seqlens and block_table must be 4-byte aligned");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || num_pages <= 0 || page_size <= 0 || max_pages <= 0 || d <= 0)
+    return fail(FA_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d num_pages=%d page_size=%d max_pages=%d d=%d)",
+                B, Hq, Hkv, num_pages, page_size, max_pages, d);
+  if (page_size % 32 != 0) return fail(FA_ERR_UNSUPPORTED, "page_size must be a multiple of 32 (got %d)", page_size);
+  const long long Lcap = (long long)max_pages * page_size;
+  if (Lcap > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "max_pages * page_size overflows int");
+  size_t cb, tb;
+  if (!mul_bytes(cb, {num_pages, Hkv, page_size, d, 2}) || !mul_bytes(tb, {B, max_pages, 4}))
     return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
-  const fa::DecodePlan p = make_plan(B, Hkv, Lcap, num_splits, Hq, d);
-  if (workspace_bytes < p.ws_bytes)
-    return fail(FA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, p.ws_bytes);
-  if (overlap(o, qb, q, qb) || overlap(o, qb, k_cache, cb) || overlap(o, qb, v_cache, cb) ||
-      overlap(workspace, p.ws_bytes, q, qb) || overlap(workspace, p.ws_bytes, k_cache, cb) ||
-      overlap(workspace, p.ws_bytes, v_cache, cb) || overlap(workspace, p.ws_bytes, o, qb))
-    return fail(FA_ERR_INVALID_ARG, "o or workspace overlaps another tensor");
-  st = check_device();
-  if (st != FA_OK) return st;
-  fa::DecodeArgs a{q, k_cache, v_cache, seqlens, o, lse, workspace, p.ws_lse_offset, B, Hq, Hkv, Lcap, d, scale,
-                   p.chunk, p.n_split, dtype};
-  hipError_t e = fa::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_decode launch: %s", hipGetErrorString(e));
-  return FA_OK;
+  return decode_impl("fa_decode_paged", q, k_pages, v_pages, block_table, seqlens, o, lse, workspace,
+                     workspace_bytes, B, Hq, Hkv, (int)Lcap, d, scale, num_splits, dtype, stream, cb, page_size,
+                     max_pages, num_pages);
 }
 
 }  // extern "C"

@@ -15,7 +15,9 @@
 // the B operand (up to 32; unused columns are zero). The next block's loads
 // are issued as soon as the current block's registers are consumed, so each
 // wave keeps a block in flight while it computes. The chunk's normalised
-// output and LSE go to the workspace.
+// output and LSE go to the workspace. The cache is either one contiguous
+// slab per (sequence, kv-head) or a set of fixed-size pages reached through a
+// per-sequence page table.
 // Combine kernel: per (b, h), merge the chunks of sequence b with the LSE form
 // of the softmax-merge identity ("The math of Flash Attention", unite.ai).
 #include "fa_launch.h"
@@ -67,11 +69,23 @@ __device__ inline u32x4 vt_tr_operand(const char* __restrict__ vl, int mt, int G
   return out;
 }
 
-template <int DT, int D>
-__global__ __launch_bounds__(64, 8) void fa_decode_split_kernel(
+// Where the cache rows live. Contiguous: [B, Hkv, Lcap, D]. Paged: pages of
+// `page` rows, [num_pages, Hkv, page, D], logical row j of sequence b in page
+// table[b * max_pages + j / page] ("Paged attention", cabseo.com).
+struct PageMap {
+  const int32_t* table;
+  int page, max_pages, num_pages;
+  int shift;  // log2(page) when page is a power of two, else -1
+};
+
+// One wave per workgroup. The d = 128 kernel is asked to keep its register
+// use down so that several chunks stay in flight per SIMD; the d = 64 kernel
+// needs no such hint (forcing it makes the compiler spill).
+template <int DT, int D, bool PAGED>
+__global__ __launch_bounds__(64, D == 128 ? 8 : 1) void fa_decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ seqlens, float* __restrict__ ws_o, float* __restrict__ ws_lse, int Hq, int Hkv,
-    int Lcap, int chunk, int n_split, float scale_log2) {
+    int Lcap, int chunk, int n_split, float scale_log2, PageMap pm) {
   constexpr int KS = D / 16, MT = D / 32, CPR = D / 8;
   using V = VBlock<D>;
   __shared__ __attribute__((aligned(16))) char vl[V::BYTES];
@@ -86,8 +100,38 @@ __global__ __launch_bounds__(64, 8) void fa_decode_split_kernel(
   const int lane = threadIdx.x, half = lane >> 5;
   const int col = lane & 31;  // q-head within the group (B-operand column)
   const size_t bg = (size_t)b * Hkv + g;
-  const uint16_t* kp = kc + (bg * Lcap + k0) * D;
-  const uint16_t* vp = vc + (bg * Lcap + k0) * D;
+
+  // Page entries of this chunk, 64 at a time, one per lane; a block of 32
+  // rows never straddles two pages (page is a multiple of 32). An entry
+  // outside [0, num_pages) is not followed (page 0 is read instead) and
+  // poisons this chunk's result.
+  int pg_lane = 0, pg_base = -(1 << 30);
+  bool bad = false;
+  auto page_of = [&](int row) -> int {  // row: logical cache row, wave-uniform
+    const int idx = pm.shift >= 0 ? row >> pm.shift : row / pm.page;
+    if (idx - pg_base >= 64 || idx < pg_base) {
+      pg_base = idx;
+      const int e = idx + lane;
+      pg_lane = (e < pm.max_pages) ? pm.table[(size_t)b * pm.max_pages + e] : 0;
+    }
+    int pg = __builtin_amdgcn_readlane(pg_lane, idx - pg_base);
+    if (pg < 0 || pg >= pm.num_pages) {
+      bad = true;
+      pg = 0;
+    }
+    return pg;
+  };
+  // Element offset of the first cache row of the 32-row block at chunk
+  // offset j0 (the same for K and V).
+  auto block_off = [&](int j0) -> size_t {
+    if constexpr (PAGED) {
+      const int row = k0 + j0;
+      const int within = pm.shift >= 0 ? row & (pm.page - 1) : row % pm.page;
+      return (((size_t)page_of(row) * Hkv + g) * pm.page + within) * D;
+    } else {
+      return (bg * Lcap + k0 + j0) * D;
+    }
+  };
 
   u32x4 qop[KS];
 #pragma unroll
@@ -110,17 +154,20 @@ __global__ __launch_bounds__(64, 8) void fa_decode_split_kernel(
   // masked to -inf, so they contribute 0); no row past L is touched.
   u32x4 ka[KS];         // K: lane holds key l%32, d chunk 2ks + l/32
   u32x4 vr[V::PER_LANE];  // V: chunk lane + 64i of the row-major block
+  size_t boff = block_off(0);  // offset of the block being loaded
   auto load_k = [&](int j0) {
-    const int row = min(j0 + col, n - 1);
+    const uint16_t* kp = kc + boff;
+    const int row = min(col, n - 1 - j0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       ka[ks] = *reinterpret_cast<const u32x4*>(kp + (size_t)row * D + 16 * ks + 8 * half);
   };
   auto load_v = [&](int j0) {
+    const uint16_t* vp = vc + boff;
 #pragma unroll
     for (int i = 0; i < V::PER_LANE; ++i) {
       const int ci = lane + 64 * i;
-      const int row = min(j0 + ci / CPR, n - 1);
+      const int row = min(ci / CPR, n - 1 - j0);
       vr[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)row * D + (ci % CPR) * 8);
     }
   };
@@ -137,7 +184,10 @@ __global__ __launch_bounds__(64, 8) void fa_decode_split_kernel(
     for (int r = 0; r < 16; ++r) sacc[0][r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) sacc[0] = mfma32<DT>(ka[ks], qop[ks], sacc[0]);
-    if (more) load_k(j0 + kBlk);
+    if (more) {
+      boff = block_off(j0 + kBlk);
+      load_k(j0 + kBlk);
+    }
     // ---- V block to LDS (previous block's transposed reads are complete:
     // every LDS read of this wave returned before its MFMA issued)
 #pragma unroll
@@ -165,7 +215,7 @@ __global__ __launch_bounds__(64, 8) void fa_decode_split_kernel(
   }
 
   // ---- chunk result: normalised O (fp32) and LSE to the workspace
-  const float l_tot = halves_sum(l_run);
+  const float l_tot = bad ? __builtin_nanf("") : halves_sum(l_run);
   if (col < grp) {
     const size_t row = ((size_t)b * Hq + g * grp + col) * n_split + s;
     const float inv = 1.f / l_tot;  // l_tot > 0: the chunk holds at least one key
@@ -253,9 +303,17 @@ template <int DT, int D>
 hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
   float* ws_o = reinterpret_cast<float*>(a.workspace);
   float* ws_lse = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + a.ws_lse_offset);
-  hipLaunchKernelGGL((fa_decode_split_kernel<DT, D>), dim3(a.n_split, a.Hkv, a.B), dim3(64), 0, stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.seqlens, ws_o,
-                     ws_lse, a.Hq, a.Hkv, a.Lcap, a.chunk, a.n_split, a.scale * kLog2e);
+  int shift = -1;
+  if (a.page_size > 0 && (a.page_size & (a.page_size - 1)) == 0) shift = __builtin_ctz((unsigned)a.page_size);
+  const PageMap pm{a.block_table, a.page_size, a.max_pages, a.num_pages, shift};
+  if (a.block_table != nullptr)
+    hipLaunchKernelGGL((fa_decode_split_kernel<DT, D, true>), dim3(a.n_split, a.Hkv, a.B), dim3(64), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.seqlens, ws_o,
+                       ws_lse, a.Hq, a.Hkv, a.Lcap, a.chunk, a.n_split, a.scale * kLog2e, pm);
+  else
+    hipLaunchKernelGGL((fa_decode_split_kernel<DT, D, false>), dim3(a.n_split, a.Hkv, a.B), dim3(64), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.seqlens, ws_o,
+                       ws_lse, a.Hq, a.Hkv, a.Lcap, a.chunk, a.n_split, a.scale * kLog2e, pm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fa_decode_combine_kernel<DT, D>), dim3(a.B * a.Hq), dim3(64), 0, stream, ws_o, ws_lse,

@@ -41,6 +41,10 @@ struct DecodeArgs {
   float scale;
   int chunk, n_split;
   int dtype;
+  // Paged cache (block_table != nullptr): k_cache / v_cache are
+  // [num_pages, Hkv, page_size, d] and Lcap = max_pages * page_size.
+  const int32_t* block_table;
+  int page_size, max_pages, num_pages;
 };
 
 constexpr int kDecodeTileRows = 128;

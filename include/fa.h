@@ -123,6 +123,44 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, con
                     int B, int Hq, int Hkv, int Lcap, int d, float scale, int num_splits,
                     int dtype, void* stream);
 
+/*
+ * fa_decode_paged - fa_decode with the KV cache held in fixed-size pages
+ * reached through a per-sequence page table.
+ *
+ * Source: "Advanced techniques for enhancing LLM throughput" (cabseo.com),
+ * section "Paged attention": the cache of each sequence is split into pages,
+ * in the manner of operating-system paging, so that caches of different and
+ * growing lengths do not fragment memory, and attention walks a sequence's
+ * cache page by page. The arithmetic, the split along the keys and the merge
+ * are those of fa_decode.
+ *
+ *   q        [B, Hq, d]                          input, dtype
+ *   k_pages  [num_pages, Hkv, page_size, d]      input, dtype: page p holds,
+ *            per kv-head, page_size consecutive cache rows of one sequence
+ *   v_pages  [num_pages, Hkv, page_size, d]      input, dtype (same layout)
+ *   block_table [B, max_pages] int32, device memory: logical cache row j of
+ *            sequence b is row j % page_size of page
+ *            block_table[b * max_pages + j / page_size]. Only the entries that
+ *            cover rows [0, seqlens[b]) are followed. An entry outside
+ *            [0, num_pages) is not followed (no memory outside k_pages /
+ *            v_pages is read); O and LSE of that sequence come out NaN.
+ *   seqlens  [B] int32, device memory; clamped to [0, max_pages * page_size].
+ *   o, lse   as in fa_decode
+ *   workspace, workspace_bytes: at least
+ *            fa_decode_workspace_bytes(B, Hq, Hkv, max_pages * page_size, d,
+ *            num_splits) bytes, 256-byte aligned, owned by the caller.
+ *   page_size   a multiple of 32
+ *   d, scale, num_splits, dtype, stream: as in fa_decode.
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED (page_size not a
+ * multiple of 32, or as in fa_decode) or FA_ERR_HIP.
+ */
+fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                          const int32_t* block_table, const int32_t* seqlens, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                          int num_pages, int page_size, int max_pages, int d, float scale,
+                          int num_splits, int dtype, void* stream);
+
 /* Static text for a status code. */
 const char* fa_status_string(int status);
 

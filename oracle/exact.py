@@ -21,6 +21,10 @@ design notes of the repository):
   * a row with no visible key: O = 0 and LSE = -inf.
   * decode (throughput page, "Memory requirements"): the new token of
     sequence b attends, unmasked, to cache rows [0, L_b).
+  * paged decode (throughput page, "Paged attention"): the cache of a
+    sequence lives in fixed-size pages found through a per-sequence page
+    table; logical row j is row j % P of page table[b, j // P]. A page-table
+    entry that names no page makes that sequence's output NaN.
 
 This module is test infrastructure. Only tests, the smoke check and the CPU
 baseline of the benchmark may use it.
@@ -141,5 +145,43 @@ def decode(q, k_cache, v_cache, seqlens, scale):
             o, lse = attention_head(np.asarray(q[b, h], np.float64)[None, :],
                                     np.asarray(k_cache[b, g, :n], np.float64),
                                     np.asarray(v_cache[b, g, :n], np.float64), scale, False)
+            O[b, h], L[b, h] = o[0], lse[0]
+    return O, L
+
+
+def paged_rows(table_row, n, P):
+    """Page id and row within the page of logical cache rows 0..n-1."""
+    rows = np.arange(n)
+    return np.asarray(table_row, np.int64)[rows // P], rows % P
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seqlens, scale):
+    """Decode against a paged cache.
+
+    q [B,Hq,d]; pages [num_pages,Hkv,P,d]; block_table [B,max_pages];
+    seqlens [B] (clamped to [0, max_pages*P]). The logical cache rows of each
+    sequence are gathered through its page table, then attended to exactly as
+    in ``decode``. If a page needed for rows [0, L_b) is outside
+    [0, num_pages), O and LSE of sequence b are NaN.
+    """
+    B, Hq, d = q.shape
+    num_pages, Hkv, P, _ = k_pages.shape
+    max_pages = block_table.shape[1]
+    Lcap = max_pages * P
+    O = np.zeros((B, Hq, v_pages.shape[3]), np.float64)
+    L = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = int(min(max(int(seqlens[b]), 0), Lcap))
+        ids = np.asarray(block_table[b, : (n + P - 1) // P], np.int64)
+        if np.any((ids < 0) | (ids >= num_pages)):
+            O[b] = np.nan
+            L[b] = np.nan
+            continue
+        pages, within = paged_rows(ids, n, P)
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            k = np.asarray(k_pages[pages, g, within], np.float64)
+            v = np.asarray(v_pages[pages, g, within], np.float64)
+            o, lse = attention_head(np.asarray(q[b, h], np.float64)[None, :], k, v, scale, False)
             O[b, h], L[b, h] = o[0], lse[0]
     return O, L

@@ -311,9 +311,53 @@ def pin_sampled_rows_match_full():
         assert np.abs(Os - O[rows]).max() <= TOL and np.abs(Ls - L[rows]).max() <= TOL
 
 
+def pin_paged_decode_is_decode():
+    # Scatter a cache into pages by hand, in a shuffled page order; following
+    # the page table must give back exactly the contiguous-cache decode.
+    r = _rng(25)
+    B, Hq, Hkv, P, max_pages, d = 3, 4, 2, 4, 5, 8
+    Lcap = P * max_pages
+    lens = np.array([1, 9, 20])
+    q = r.standard_normal((B, Hq, d))
+    kc = r.standard_normal((B, Hkv, Lcap, d))
+    vc = r.standard_normal((B, Hkv, Lcap, d))
+    for b in range(B):
+        kc[b, :, lens[b]:] = np.nan
+        vc[b, :, lens[b]:] = np.nan
+    num_pages = B * max_pages + 2
+    order = r.permutation(num_pages)
+    table = np.zeros((B, max_pages), np.int64)
+    kp = np.full((num_pages, Hkv, P, d), np.nan)
+    vp = np.full((num_pages, Hkv, P, d), np.nan)
+    for b in range(B):
+        for j in range(max_pages):
+            pid = order[b * max_pages + j]
+            table[b, j] = pid
+            for g in range(Hkv):
+                for t in range(P):
+                    kp[pid, g, t] = kc[b, g, j * P + t]
+                    vp[pid, g, t] = vc[b, g, j * P + t]
+    O, L = oracle.decode(q, kc, vc, lens, 0.3)
+    Op, Lp = oracle.decode_paged(q, kp, vp, table, lens, 0.3)
+    assert np.array_equal(O, Op) and np.array_equal(L, Lp)
+    # entries past the pages a sequence needs are never followed
+    t2 = table.copy()
+    t2[0, 1:] = -5
+    t2[1, 3:] = num_pages + 7
+    Op2, Lp2 = oracle.decode_paged(q, kp, vp, t2, lens, 0.3)
+    assert np.array_equal(O, Op2) and np.array_equal(L, Lp2)
+    # a needed entry that names no page poisons that sequence only
+    t3 = table.copy()
+    t3[2, 4] = num_pages
+    Op3, Lp3 = oracle.decode_paged(q, kp, vp, t3, lens, 0.3)
+    assert np.all(np.isnan(Op3[2])) and np.all(np.isnan(Lp3[2]))
+    assert np.array_equal(Op3[:2], O[:2]) and np.array_equal(Lp3[:2], L[:2])
+
+
 ALL_PINS = [
     pin_brute_force, pin_single_key_and_causal_row0, pin_two_keys, pin_golden_fixtures,
     pin_zero_query, pin_rows_sum_to_one, pin_merge_identity, pin_shift_invariance,
     pin_permutation, pin_convex_hull, pin_causal_is_prefix, pin_gqa_is_repeated_mha,
     pin_decode_is_single_query, pin_lse_library, pin_sampled_rows_match_full,
+    pin_paged_decode_is_decode,
 ]

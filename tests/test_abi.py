@@ -29,7 +29,8 @@ def test_library_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"fa_fwd", "fa_decode", "fa_decode_workspace_bytes", "fa_status_string", "fa_last_error"} <= set(names)
+    assert {"fa_fwd", "fa_decode", "fa_decode_paged", "fa_decode_workspace_bytes", "fa_status_string",
+            "fa_last_error"} <= set(names)
     raw = ctypes.CDLL(fa.lib_path())
     for n in names:
         assert hasattr(raw, n), f"{n} declared in fa.h but not exported"
@@ -106,6 +107,32 @@ def dec(**kw):
 ])
 def test_decode_rejects_before_launch(kw, status):
     st = dec(**kw)
+    assert st == status, (st, fa.fa_last_error())
+
+
+def dec_paged(**kw):
+    a = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, table=FAKE + 0x2800000, seqlens=FAKE + 0x3000000,
+             o=FAKE + 0x3100000, lse=None, ws=FAKE + 0x4000000, ws_bytes=1 << 30, B=2, Hq=8, Hkv=2,
+             num_pages=64, page_size=128, max_pages=8, d=128, scale=0.088, num_splits=0, dtype=0, stream=None)
+    a.update(kw)
+    return fa.fa_decode_paged(a["q"], a["k"], a["v"], a["table"], a["seqlens"], a["o"], a["lse"], a["ws"],
+                              a["ws_bytes"], a["B"], a["Hq"], a["Hkv"], a["num_pages"], a["page_size"],
+                              a["max_pages"], a["d"], a["scale"], a["num_splits"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(table=None), fa.FA_ERR_INVALID_ARG),
+    (dict(table=FAKE + 0x2800002), fa.FA_ERR_INVALID_ARG),  # table not 4-byte aligned
+    (dict(num_pages=0), fa.FA_ERR_INVALID_ARG),
+    (dict(max_pages=0), fa.FA_ERR_INVALID_ARG),
+    (dict(page_size=48), fa.FA_ERR_UNSUPPORTED),            # not a multiple of 32
+    (dict(page_size=1 << 20, max_pages=1 << 12), fa.FA_ERR_INVALID_ARG),  # capacity overflows int
+    (dict(ws_bytes=16), fa.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(o=FAKE + 0x1000010), fa.FA_ERR_INVALID_ARG),      # o inside k_pages
+])
+def test_decode_paged_rejects_before_launch(kw, status):
+    st = dec_paged(**kw)
     assert st == status, (st, fa.fa_last_error())
 
 

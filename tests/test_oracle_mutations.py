@@ -125,6 +125,16 @@ def _decode_off_by_one(q, k_cache, v_cache, seqlens, scale):
     return _real_decode(q, k_cache, v_cache, np.maximum(np.asarray(seqlens) - 1, 0), scale)
 
 
+def _paged_rows_swapped(table_row, n, P):
+    rows = np.arange(n)
+    return np.asarray(table_row, np.int64)[rows % P], rows // P
+
+
+def _paged_rows_ignore_table(table_row, n, P):
+    rows = np.arange(n)
+    return rows // P, rows % P
+
+
 def _scale_not_rounded(scale):
     return float(scale)
 
@@ -144,6 +154,8 @@ MUTATIONS = [
     ("decode_whole_cache", oracle, "decode", _decode_whole_cache),
     ("decode_off_by_one", oracle, "decode", _decode_off_by_one),
     ("scale_not_fp32", oe, "as_fp32_scale", _scale_not_rounded),
+    ("paged_rows_swapped", oe, "paged_rows", _paged_rows_swapped),
+    ("paged_rows_ignore_table", oe, "paged_rows", _paged_rows_ignore_table),
 ]
 
 
