@@ -27,7 +27,7 @@ import numpy as np
 __all__ = [
     "BF16", "FP16", "Q_ID", "K_ID", "V_ID",
     "round_to_bits", "bits_to_f64", "slab", "prefill_inputs",
-    "decode_lengths", "decode_inputs", "paged_layout", "sample_rows", "CONFIGS",
+    "decode_lengths", "decode_inputs", "paged_layout", "varlen_inputs", "sample_rows", "CONFIGS",
 ]
 
 BF16 = "bf16"
@@ -36,7 +36,7 @@ Q_ID, K_ID, V_ID = 0, 1, 2
 BF16_NAN_BITS = 0x7FC0
 FP16_NAN_BITS = 0x7E00
 
-# The five workloads: shapes, dtype, mask. Seed of config k is k.
+# The workloads: shapes, dtype, mask. Seed of config k is k.
 CONFIGS = {
     "tiny_mha_n128": dict(seed=1, B=1, Hq=8, Hkv=8, N=128, d=64, dtype=BF16, causal=(False,)),
     "mha_n4096_fp16": dict(seed=2, B=2, Hq=8, Hkv=8, N=4096, d=64, dtype=FP16, causal=(False, True)),
@@ -45,6 +45,10 @@ CONFIGS = {
                             sample_rows=256),
     "decode_32seq_gqa": dict(seed=5, B=32, Hq=32, Hkv=8, Lcap=32768, d=128, dtype=BF16,
                       len_lo=1024, len_hi=32768),
+    # Packed prefill of 16 Llama-3-shaped sequences, lengths U[512, 8192]
+    # (drawn like the decode lengths), causal, no padding.
+    "llama3_8b_gqa_varlen": dict(seed=6, B=16, Hq=32, Hkv=8, d=128, dtype=BF16, causal=(True,),
+                          len_lo=512, len_hi=8192),
 }
 
 
@@ -168,6 +172,26 @@ def paged_layout(k_cache: np.ndarray, v_cache: np.ndarray, page_size: int, seed:
         out[name] = pages
     out.update(block_table=table, page_size=page_size)
     return out
+
+
+def varlen_inputs(seed: int, lens_q, lens_k, Hq: int, Hkv: int, d: int, dtype: str) -> dict:
+    """A packed batch: q [Hq, total_q, d], k/v [Hkv, total_k, d] with sequence
+    b's rows drawn as the slabs of batch index b (the same values
+    ``prefill_inputs`` gives sequence b), plus cu_seqlens [B+1] int32."""
+    lens_q = np.asarray(lens_q, np.int64)
+    lens_k = np.asarray(lens_k, np.int64)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    q = np.empty((Hq, int(cu_q[-1]), d), np.uint16)
+    k = np.empty((Hkv, int(cu_k[-1]), d), np.uint16)
+    v = np.empty((Hkv, int(cu_k[-1]), d), np.uint16)
+    for b in range(len(lens_q)):
+        for h in range(Hq):
+            q[h, cu_q[b]:cu_q[b + 1]] = slab(seed, Q_ID, b, h, int(lens_q[b]), d, dtype)
+        for g in range(Hkv):
+            k[g, cu_k[b]:cu_k[b + 1]] = slab(seed, K_ID, b, g, int(lens_k[b]), d, dtype)
+            v[g, cu_k[b]:cu_k[b + 1]] = slab(seed, V_ID, b, g, int(lens_k[b]), d, dtype)
+    return dict(q=q, k=k, v=v, cu_q=cu_q, cu_k=cu_k, dtype=dtype)
 
 
 def sample_rows(seed: int, head: int, N: int, count: int = 256) -> np.ndarray:

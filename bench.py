@@ -22,7 +22,9 @@ Other modes (used to take rocprofv3 counter readings):
   --config NAME      a single configuration (tiny_mha_n128, mha_n4096_fp16,
                      mha_n4096_fp16_causal, llama3_8b_gqa_n8192, llama3_8b_gqa_n131072,
                      decode_32seq_gqa, decode_32seq_gqa_paged: the same decode with
-                     the cache in 128-row pages in a shuffled page order)
+                     the cache in 128-row pages in a shuffled page order,
+                     llama3_8b_gqa_varlen: packed causal prefill of 16
+                     sequences with lengths U[512, 8192])
 """
 from __future__ import annotations
 
@@ -124,6 +126,34 @@ class Prefill:
 
     def __call__(self):
         self.fa.attention(self.q, self.k, self.v, causal=self.causal, out=self.o, lse=self.lse)
+
+
+class PrefillVarlen:
+    """Packed causal prefill: 16 Llama-3-shaped sequences of seeded lengths,
+    one slab per head, no padding. FLOPs sum the per-sequence counts."""
+
+    def __init__(self, fa, name="llama3_8b_gqa_varlen"):
+        import torch
+        c = ai.CONFIGS[name]
+        self.fa = fa
+        t0 = time.time()
+        self.lens = ai.decode_lengths(c["seed"], c["B"], c["len_lo"], c["len_hi"])
+        x = ai.varlen_inputs(c["seed"], self.lens, self.lens, c["Hq"], c["Hkv"], c["d"], c["dtype"])
+        self.q, self.k, self.v = to_dev(x["q"], c["dtype"]), to_dev(x["k"], c["dtype"]), to_dev(x["v"], c["dtype"])
+        self.cu_q = torch.from_numpy(x["cu_q"]).cuda()
+        self.cu_k = torch.from_numpy(x["cu_k"]).cuda()
+        del x
+        self.max_q = int(self.lens.max())
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((c["Hq"], self.q.shape[1]), dtype=torch.float32, device="cuda")
+        self.flops = sum(prefill_flops(1, c["Hq"], int(n), int(n), c["d"], True) for n in self.lens)
+        self.bytes = sum(prefill_bytes(1, c["Hq"], c["Hkv"], int(n), int(n), c["d"]) for n in self.lens)
+        log(f"[bench] {name}: {len(self.lens)} sequences, {int(self.lens.sum())} tokens, "
+            f"inputs ready in {time.time() - t0:.1f}s")
+
+    def __call__(self):
+        self.fa.attention_varlen(self.q, self.k, self.v, self.cu_q, self.cu_k, self.max_q, causal=True,
+                                 out=self.o, lse=self.lse)
 
 
 class Decode:
@@ -246,6 +276,24 @@ def cpu_baseline_prefill(name="llama3_8b_gqa_n8192", heads=8):
                       f"(float64 NumPy, score matrix materialised); {elapsed:.1f}s"}
 
 
+def cpu_baseline_varlen(name="llama3_8b_gqa_varlen", seqs=2, heads=4):
+    """The oracle's packed prefill on the first `seqs` sequences, `heads`
+    q-heads each (all rows, causal): TFLOP/s by the GPU's FLOP convention."""
+    import oracle
+    c = ai.CONFIGS[name]
+    lens = ai.decode_lengths(c["seed"], c["B"], c["len_lo"], c["len_hi"])[:seqs]
+    x = ai.varlen_inputs(c["seed"], lens, lens, heads, max(1, heads // (c["Hq"] // c["Hkv"])), c["d"], c["dtype"])
+    f = lambda a: ai.bits_to_f64(a, c["dtype"])
+    q, k, v = f(x["q"]), f(x["k"]), f(x["v"])
+    t0 = time.perf_counter()
+    oracle.attention_varlen(q, k, v, x["cu_q"], x["cu_k"], 1.0 / math.sqrt(c["d"]), causal=True)
+    elapsed = time.perf_counter() - t0
+    flops = sum(prefill_flops(1, heads, int(n), int(n), c["d"], True) for n in lens)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cpu_cores_used(), "kind": "oracle",
+            "sample": f"first {seqs} of {c['B']} sequences (lengths {lens.tolist()}), {heads} of 32 q-heads, "
+                      f"all rows, causal (float64 NumPy); {elapsed:.1f}s"}
+
+
 def cpu_baseline_decode(name="decode_32seq_gqa", seqs=32, page_size=0):
     """The oracle's decode (paged decode when page_size > 0, through a
     shuffled page table) on the first `seqs` sequences: GB/s by the same byte
@@ -324,17 +372,19 @@ def main():
     fa.load_library()
 
     cfg = args.config
-    run_prefill = cfg in ("default", "tiny_mha_n128", "mha_n4096_fp16", "mha_n4096_fp16_causal", "llama3_8b_gqa_n8192", "llama3_8b_gqa_n131072")
+    run_prefill = cfg in ("default", "tiny_mha_n128", "mha_n4096_fp16", "mha_n4096_fp16_causal", "llama3_8b_gqa_n8192",
+                          "llama3_8b_gqa_n131072", "llama3_8b_gqa_varlen")
     run_decode = cfg in ("default", "decode_32seq_gqa", "decode_32seq_gqa_paged")
     paged = cfg == "decode_32seq_gqa_paged"
     if not (run_prefill or run_decode):
         raise SystemExit(f"unknown --config {cfg}")
     pname = "llama3_8b_gqa_n8192" if cfg == "default" else cfg.replace("_causal", "")
-    causal = cfg in ("default", "llama3_8b_gqa_n8192", "llama3_8b_gqa_n131072", "mha_n4096_fp16_causal")
+    causal = cfg in ("default", "llama3_8b_gqa_n8192", "llama3_8b_gqa_n131072", "mha_n4096_fp16_causal",
+                     "llama3_8b_gqa_varlen")
     parts = []
     pre = dec = None
     if run_prefill:
-        pre = Prefill(fa, pname, causal)
+        pre = PrefillVarlen(fa) if cfg == "llama3_8b_gqa_varlen" else Prefill(fa, pname, causal)
         parts.append(pre)
     if run_decode:
         dec = DecodePaged(fa, num_splits=args.num_splits) if paged else Decode(fa, num_splits=args.num_splits)
@@ -375,7 +425,9 @@ def main():
                    "kernel_source_sha256": kernel_source_hash()},
     })
     if not args.no_cpu_baseline:
-        if pre is not None and pname == "llama3_8b_gqa_n8192":
+        if cfg == "llama3_8b_gqa_varlen":
+            out["cpu_baseline"] = cpu_baseline_varlen()
+        elif pre is not None and pname == "llama3_8b_gqa_n8192":
             out["cpu_baseline"] = cpu_baseline_prefill()
             if dec is not None:
                 out["decode"]["cpu_baseline"] = cpu_baseline_decode()

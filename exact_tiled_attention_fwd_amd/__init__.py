@@ -6,10 +6,12 @@ runs in the HIP kernels of that library; this module only marshals arguments.
 PyTorch supplies device memory and the current stream.
 
 Raw entry points, same names and argument order as the C header:
-    fa_fwd, fa_decode, fa_decode_paged, fa_decode_workspace_bytes,
+    fa_fwd, fa_fwd_varlen, fa_decode, fa_decode_paged, fa_decode_workspace_bytes,
     fa_status_string, fa_last_error, fa_abi_version
 Tensor-level helpers:
     attention(q, k, v, causal=False, scale=None) -> (o, lse)
+    attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                     causal=False, scale=None) -> (o, lse)
     decode(q, k_cache, v_cache, seqlens, scale=None, num_splits=0) -> (o, lse)
     decode_paged(q, k_pages, v_pages, block_table, seqlens, scale=None,
                  num_splits=0) -> (o, lse)
@@ -28,8 +30,8 @@ import torch  # loads the HIP runtime that libfa.so then binds to
 __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
     "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FAError", "lib_path", "load_library",
-    "fa_fwd", "fa_decode", "fa_decode_paged", "fa_decode_workspace_bytes", "fa_status_string",
-    "fa_last_error", "fa_abi_version", "attention", "decode", "decode_paged", "dtype_code",
+    "fa_fwd", "fa_fwd_varlen", "fa_decode", "fa_decode_paged", "fa_decode_workspace_bytes", "fa_status_string",
+    "fa_last_error", "fa_abi_version", "attention", "attention_varlen", "decode", "decode_paged", "dtype_code",
 ]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
@@ -73,6 +75,8 @@ def load_library():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd.restype = i
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_varlen.restype = i
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
     lib.fa_decode.restype = i
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, i, i, vp]
@@ -105,6 +109,13 @@ def _raise_for(status: int):
 def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, stream) -> int:
     """Call the C ``fa_fwd`` with integer device addresses; returns the status."""
     return load_library().fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, stream)
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q, total_k, max_seqlen_q,
+                  d, scale, causal, dtype, stream) -> int:
+    """Call the C ``fa_fwd_varlen`` with integer device addresses; returns the status."""
+    return load_library().fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q, total_k,
+                                        max_seqlen_q, d, scale, causal, dtype, stream)
 
 
 def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, workspace_bytes,
@@ -189,6 +200,39 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
     with torch.cuda.device(dev):
         st = fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
                     float(scale), int(bool(causal)), dtype_code(q.dtype), _stream(dev))
+    _raise_for(st)
+    return out, lse
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
+                     scale: float | None = None, out=None, lse=None):
+    """Packed variable-length batch: q [Hq,total_q,d], k/v [Hkv,total_k,d],
+    cu_seqlens_* int32 [B+1] on the device, max_seqlen_q a host int."""
+    _check_tensor("q", q, 3)
+    dev = q.device
+    _check_tensor("k", k, 3, dev)
+    _check_tensor("v", v, 3, dev)
+    _check_tensor("cu_seqlens_q", cu_seqlens_q, 1, dev)
+    _check_tensor("cu_seqlens_k", cu_seqlens_k, 1, dev)
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "cu_seqlens must be int32")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "q, k and v must share a dtype")
+    Hq, total_q, d = q.shape
+    Hkv, total_k, dk = k.shape
+    B = cu_seqlens_q.shape[0] - 1
+    if dk != d or tuple(v.shape) != tuple(k.shape) or cu_seqlens_k.shape[0] != B + 1 or B < 1:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "shape mismatch between q, k, v and cu_seqlens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        st = fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                           B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), d, float(scale), int(bool(causal)),
+                           dtype_code(q.dtype), _stream(dev))
     _raise_for(st)
     return out, lse
 

@@ -144,9 +144,46 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
     return fail(FA_ERR_INVALID_ARG, "lse overlaps another tensor");
   st = check_device();
   if (st != FA_OK) return st;
-  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype};
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, nullptr, nullptr, 0, 0, 0};
   hipError_t e = fa::launch_fwd(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd launch: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k,
+                         int max_seqlen_q, int d, float scale, int causal, int dtype, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k)
+    return fail(FA_ERR_INVALID_ARG, "q, k, v, o, cu_seqlens_q and cu_seqlens_k must be non-null");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(FA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
+  if (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return fail(FA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must be 4-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || total_q <= 0 || total_k <= 0 || max_seqlen_q <= 0 || d <= 0)
+    return fail(FA_ERR_INVALID_ARG,
+                "sizes must be positive (B=%d Hq=%d Hkv=%d total_q=%d total_k=%d max_seqlen_q=%d d=%d)", B, Hq, Hkv,
+                total_q, total_k, max_seqlen_q, d);
+  if (max_seqlen_q > total_q) return fail(FA_ERR_INVALID_ARG, "max_seqlen_q=%d exceeds total_q=%d", max_seqlen_q, total_q);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
+  fa_status st = check_common(d, dtype, scale, Hq, Hkv);
+  if (st != FA_OK) return st;
+  size_t qb, kb, lb;
+  if (!mul_bytes(qb, {Hq, total_q, d, 2}) || !mul_bytes(kb, {Hkv, total_k, d, 2}) || !mul_bytes(lb, {Hq, total_q, 4}))
+    return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
+  if ((long long)((max_seqlen_q + fa::kFwdBlockRows - 1) / fa::kFwdBlockRows) * B * Hq > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "grid too large");
+  if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb))
+    return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
+  if (lse && (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) || overlap(lse, lb, o, qb)))
+    return fail(FA_ERR_INVALID_ARG, "lse overlaps another tensor");
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, 0, 0, d, scale, causal, dtype,
+                cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q};
+  hipError_t e = fa::launch_fwd(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd_varlen launch: %s", hipGetErrorString(e));
   return FA_OK;
 }
 

@@ -131,40 +131,44 @@ struct DmaSpread {
   }
 };
 
-template <int DT, bool CAUSAL>
+template <int DT, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_d128_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Nq, int Nk,
-    float scale_log2, int n_qt) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Nq_all, int Nk_all,
+    float scale_log2, int n_qt, Varlen vlen) {
   constexpr int D = kD, ROWS = kRows;
   __shared__ __attribute__((aligned(1024))) char smem[2 * kSlots * kTile];
   char* const kring = smem;                   // K tile t in slot t % 3
   char* const vring = smem + kSlots * kTile;  // V tile t in slot t % 3
 
-  const Work wk = map_work(blockIdx.x, B, Hq, Hkv, n_qt);
+  const Work wk = VARLEN ? map_work_packed(blockIdx.x, B, Hq, Hkv, n_qt) : map_work(blockIdx.x, B, Hq, Hkv, n_qt);
+  const Slabs sl = slabs_of<VARLEN, D>(wk, q, k, v, o, lse, Hq, Hkv, Nq_all, Nk_all, vlen);
+  const int Nq = sl.Nq, Nk = sl.Nk;
+  const int q0 = wk.qt * kBM;
+  if (VARLEN && q0 >= Nq) return;  // past this sequence's rows (the whole workgroup)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int grp = wave >> 2;  // 0: matrix cores first; 1: softmax first
-  const int q0 = wk.qt * kBM;
   const int q0w = q0 + 32 * wave;  // first query row of this wave
   const int off = Nk - Nq;         // causal: key j visible to query i iff j <= i + off
 
-  const size_t bh = (size_t)wk.b * Hq + wk.h;
-  const size_t bg = (size_t)wk.b * Hkv + wk.g;
-  const uint16_t* qp = q + bh * Nq * D;
-  const uint16_t* kp = k + bg * Nk * D;
-  const uint16_t* vp = v + bg * Nk * D;
+  const uint16_t* qp = sl.q;
+  const uint16_t* kp = sl.k;
+  const uint16_t* vp = sl.v;
 
-  // Key tiles this workgroup visits.
+  // Key tiles this workgroup visits (none for rows that see no key).
   int n_kv = (Nk + ROWS - 1) / ROWS;
   if (CAUSAL) {
     const int last_key = min(q0 + kBM, Nq) - 1 + off;
-    n_kv = min(n_kv, last_key / ROWS + 1);
+    n_kv = last_key < 0 ? 0 : min(n_kv, last_key / ROWS + 1);
   }
   // Key tiles this wave computes on (0 if the wave has no valid query row).
   const bool wave_active = q0w < Nq;
   int wave_tiles = wave_active ? n_kv : 0;
-  if (CAUSAL && wave_active) wave_tiles = min(n_kv, (min(q0w + 31, Nq - 1) + off) / ROWS + 1);
+  if (CAUSAL && wave_active) {
+    const int last = min(q0w + 31, Nq - 1) + off;
+    wave_tiles = last < 0 ? 0 : min(n_kv, last / ROWS + 1);
+  }
 
   // Q^T operand (B operand of S^T = K Q^T), held for the whole loop.
   const int qrow = q0w + (lane & 31);
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_d128_kernel(
   const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < Nq) {
-    uint16_t* orow = o + bh * Nq * D + (size_t)qrow * D;
+    uint16_t* orow = sl.o + (size_t)qrow * D;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -332,28 +336,36 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_d128_kernel(
                          pack2<DT>(acc_o[mt][4 * i + 2] * inv, acc_o[mt][4 * i + 3] * inv)};
         *reinterpret_cast<u32x2*>(orow + d0) = w;
       }
-    if (lse != nullptr && half == 0)
-      lse[bh * Nq + qrow] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
+    if (sl.lse != nullptr && half == 0)
+      sl.lse[qrow] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
   }
 }
 
-template <int DT, bool CAUSAL>
+template <int DT, bool CAUSAL, bool VARLEN>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
-  const int n_qt = (a.Nq + kBM - 1) / kBM;
+  const int rows = VARLEN ? a.max_seqlen_q : a.Nq;
+  const int n_qt = (rows + kBM - 1) / kBM;
   const long long nblocks = (long long)n_qt * a.B * a.Hq;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa_fwd_d128_kernel<DT, CAUSAL>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+  if (nblocks == 0) return hipSuccess;
+  const Varlen vl{a.cu_q, a.cu_k, a.total_q, a.total_k};
+  hipLaunchKernelGGL((fa_fwd_d128_kernel<DT, CAUSAL, VARLEN>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_qt);
+                     a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_qt, vl);
   return hipGetLastError();
+}
+
+template <int DT, bool CAUSAL>
+hipError_t launch_v(const FwdArgs& a, hipStream_t stream) {
+  return a.cu_q != nullptr ? launch_t<DT, CAUSAL, true>(a, stream) : launch_t<DT, CAUSAL, false>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_d128(const FwdArgs& a, hipStream_t stream) {
   const bool c = a.causal != 0;
-  if (a.dtype == DT_BF16) return c ? launch_t<DT_BF16, true>(a, stream) : launch_t<DT_BF16, false>(a, stream);
-  return c ? launch_t<DT_FP16, true>(a, stream) : launch_t<DT_FP16, false>(a, stream);
+  if (a.dtype == DT_BF16) return c ? launch_v<DT_BF16, true>(a, stream) : launch_v<DT_BF16, false>(a, stream);
+  return c ? launch_v<DT_FP16, true>(a, stream) : launch_v<DT_FP16, false>(a, stream);
 }
 
 }  // namespace fa

@@ -18,6 +18,12 @@ struct FwdArgs {
   float scale;
   int causal;
   int dtype;
+  // Packed variable-length batch (cu_q != nullptr): q, o [Hq, total_q, d],
+  // k, v [Hkv, total_k, d], lse [Hq, total_q]; Nq / Nk unused; query tiles
+  // cover max_seqlen_q rows per sequence.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k, max_seqlen_q;
 };
 
 // Decode key split: chunk keys per workgroup, n_split chunks cover Lcap rows.

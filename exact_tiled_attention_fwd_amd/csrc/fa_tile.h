@@ -459,4 +459,82 @@ __device__ inline Work map_work(int L, int B, int Hq, int Hkv, int n_qt) {
   return w;
 }
 
+// Work order for packed batches, where a later query tile is not in general
+// a heavier one: sequence-major, so that one (sequence, kv-head) pair's K/V
+// is read by all its query tiles and q-heads while it sits in L2; query
+// tiles of a sequence heaviest first. When Hkv is a multiple of 8, XCD x
+// (workgroup ids L with L % 8 == x) serves the kv-heads g with g % 8 == x.
+__device__ inline Work map_work_packed(int L, int B, int Hq, int Hkv, int n_qt) {
+  const int grp = Hq / Hkv;
+  const int per_pair = n_qt * grp;
+  int s = L, x = 0, gstride = 1, goff = 0, gper = Hkv;
+  if ((Hkv & 7) == 0) {
+    x = L & 7;
+    s = L >> 3;
+    gstride = 8;
+    goff = x;
+    gper = Hkv >> 3;
+  }
+  const int p = s / per_pair, rem = s % per_pair;
+  Work w;
+  w.b = p / gper;
+  w.g = (p % gper) * gstride + goff;
+  w.qt = n_qt - 1 - rem / grp;
+  w.h = w.g * grp + rem % grp;
+  return w;
+}
+
+// ------------------------------------------------------------------ slabs
+// Packed variable-length batches: sequence b's query rows are rows
+// [cu_q[b], cu_q[b+1]) of each head's [total_q, d] slab, its keys rows
+// [cu_k[b], cu_k[b+1]) of each kv-head's [total_k, d] slab.
+struct Varlen {
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k;
+};
+
+// The slabs one workgroup reads and writes, with their row counts.
+struct Slabs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;  // null: not written
+  int Nq, Nk;
+};
+
+// Fixed layout: q, o [B, Hq, Nq, D]; k, v [B, Hkv, Nk, D]; lse [B, Hq, Nq].
+// Packed layout: offsets are clamped into [0, total] and made non-decreasing,
+// so no offset array, however wrong, leads outside the tensors.
+template <bool VARLEN, int D>
+__device__ inline Slabs slabs_of(const Work& w, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                                 float* lse, int Hq, int Hkv, int Nq, int Nk, const Varlen& vl) {
+  Slabs s;
+  if constexpr (VARLEN) {
+    const int q_lo = min(max(vl.cu_q[w.b], 0), vl.total_q);
+    const int q_hi = min(max(vl.cu_q[w.b + 1], q_lo), vl.total_q);
+    const int k_lo = min(max(vl.cu_k[w.b], 0), vl.total_k);
+    const int k_hi = min(max(vl.cu_k[w.b + 1], k_lo), vl.total_k);
+    const size_t qoff = ((size_t)w.h * vl.total_q + q_lo), koff = ((size_t)w.g * vl.total_k + k_lo);
+    s.q = q + qoff * D;
+    s.o = o + qoff * D;
+    s.lse = lse ? lse + qoff : nullptr;
+    s.k = k + koff * D;
+    s.v = v + koff * D;
+    s.Nq = q_hi - q_lo;
+    s.Nk = k_hi - k_lo;
+  } else {
+    const size_t bh = (size_t)w.b * Hq + w.h, bg = (size_t)w.b * Hkv + w.g;
+    s.q = q + bh * Nq * D;
+    s.o = o + bh * Nq * D;
+    s.lse = lse ? lse + bh * Nq : nullptr;
+    s.k = k + bg * Nk * D;
+    s.v = v + bg * Nk * D;
+    s.Nq = Nq;
+    s.Nk = Nk;
+  }
+  return s;
+}
+
 }  // namespace fa

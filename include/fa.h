@@ -80,6 +80,40 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int dtype, void* stream);
 
 /*
+ * fa_fwd_varlen - fa_fwd over a packed batch of sequences of different
+ * lengths, with no padding.
+ *
+ * Source: "Advanced techniques for enhancing LLM throughput" (cabseo.com),
+ * section "Continuous batching": requests of different lengths are batched
+ * together, and padding the short ones to the longest wastes work. Each
+ * sequence is attended to exactly as by fa_fwd (same arithmetic, same causal
+ * alignment per sequence); sequences never see each other's keys.
+ *
+ *   q      [Hq, total_q, d]   input, dtype: sequence b's query rows are rows
+ *          cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of each head's slab
+ *   k, v   [Hkv, total_k, d]  input, dtype: its keys are rows
+ *          cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1
+ *   o      [Hq, total_q, d]   output, dtype (rows of no sequence untouched)
+ *   lse    [Hq, total_q] fp32 output, may be NULL
+ *   cu_seqlens_q, cu_seqlens_k  [B+1] int32, device memory, non-decreasing
+ *          from 0. Offsets are clamped into [0, total] (and an end below its
+ *          start to the start), so no offset array can send the kernels
+ *          outside the tensors.
+ *   max_seqlen_q  upper bound on every sequence's query length: query rows
+ *          past it are not computed.
+ *   causal 0/1, per sequence bottom-right aligned (key j visible to query i
+ *          iff j <= i + Nk_b - Nq_b). A row that sees no key (a sequence with
+ *          Nk_b = 0, or causal with Nq_b > Nk_b) gets O = 0 and LSE = -inf.
+ *   B, Hq, Hkv, d, scale, dtype, stream: as in fa_fwd.
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                        int d, float scale, int causal, int dtype, void* stream);
+
+/*
  * fa_decode_workspace_bytes - bytes of device workspace fa_decode needs for
  * these sizes and this `num_splits` (0 = the library's choice). Returns 0 if
  * the sizes are invalid. The workspace holds per-split partial outputs and

@@ -13,6 +13,6 @@ random configurations are pinned only through this oracle.
 """
 from .exact import (  # noqa: F401
     as_fp32_scale, scores, visibility, softmax_rows, attention_head, attention,
-    attention_rows, decode, decode_paged,
+    attention_rows, attention_varlen, decode, decode_paged,
 )
 from .blockwise import blockwise_attention_head, merge_partials  # noqa: F401

@@ -21,6 +21,10 @@ design notes of the repository):
   * a row with no visible key: O = 0 and LSE = -inf.
   * decode (throughput page, "Memory requirements"): the new token of
     sequence b attends, unmasked, to cache rows [0, L_b).
+  * packed variable-length prefill (throughput page, "Continuous
+    batching"): sequences of different lengths share one slab per head
+    without padding; sequence b owns rows cu_q[b]..cu_q[b+1]-1 of queries and
+    cu_k[b]..cu_k[b+1]-1 of keys, and attends only to its own keys.
   * paged decode (throughput page, "Paged attention"): the cache of a
     sequence lives in fixed-size pages found through a per-sequence page
     table; logical row j is row j % P of page table[b, j // P]. A page-table
@@ -126,6 +130,38 @@ def attention_rows(q_rows, rows, k, v, scale, causal, Nq):
     with np.errstate(divide="ignore"):
         lse = np.where(l > 0, m + np.log(np.where(l > 0, l, 1.0)), -np.inf)
     return P @ v, lse
+
+
+def varlen_bounds(cu, b, total):
+    """Rows [lo, hi) of sequence b: offsets clamped into [0, total], hi >= lo."""
+    lo = min(max(int(cu[b]), 0), total)
+    hi = min(max(int(cu[b + 1]), lo), total)
+    return lo, hi
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, scale, causal=False):
+    """Packed batch: q [Hq,total_q,d], k/v [Hkv,total_k,d], cu_* [B+1].
+
+    Each sequence is ``attention`` on its own rows and keys; rows that belong
+    to no sequence stay 0 (O) and NaN (LSE)."""
+    Hq, total_q, d = q.shape
+    Hkv, total_k = k.shape[0], k.shape[1]
+    O = np.zeros((Hq, total_q, v.shape[2]), np.float64)
+    L = np.full((Hq, total_q), np.nan)
+    for b in range(len(cu_q) - 1):
+        q_lo, q_hi = varlen_bounds(cu_q, b, total_q)
+        k_lo, k_hi = varlen_bounds(cu_k, b, total_k)
+        if q_hi == q_lo:
+            continue
+        for h in range(Hq):
+            g = _kv_head(h, Hq, Hkv)
+            if k_hi == k_lo:
+                O[h, q_lo:q_hi] = 0.0
+                L[h, q_lo:q_hi] = -np.inf
+                continue
+            o, lse = attention_head(q[h, q_lo:q_hi], k[g, k_lo:k_hi], v[g, k_lo:k_hi], scale, causal)
+            O[h, q_lo:q_hi], L[h, q_lo:q_hi] = o, lse
+    return O, L
 
 
 def decode(q, k_cache, v_cache, seqlens, scale):

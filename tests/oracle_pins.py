@@ -354,10 +354,56 @@ def pin_paged_decode_is_decode():
     assert np.array_equal(Op3[:2], O[:2]) and np.array_equal(Lp3[:2], L[:2])
 
 
+def pin_varlen_is_per_sequence():
+    # A packed batch is each sequence's own attention (checked against the
+    # brute force), with no key shared across sequences.
+    r = _rng(26)
+    Hq, Hkv, d = 4, 2, 6
+    nq = [3, 0, 5, 2, 4]
+    nk = [4, 3, 5, 0, 2]          # sequence 4: causal with Nq > Nk leaves rows that see nothing
+    cu_q = np.concatenate([[0], np.cumsum(nq)])
+    cu_k = np.concatenate([[0], np.cumsum(nk)])
+    tq, tk = int(cu_q[-1]) + 2, int(cu_k[-1])   # two trailing rows belong to no sequence
+    q = r.standard_normal((Hq, tq, d))
+    k = r.standard_normal((Hkv, tk, d))
+    v = r.standard_normal((Hkv, tk, d))
+    for causal in (False, True):
+        O, L = oracle.attention_varlen(q, k, v, cu_q, cu_k, 0.45, causal)
+        for b in range(len(nq)):
+            for h in range(Hq):
+                g = h // (Hq // Hkv)
+                rows = slice(cu_q[b], cu_q[b + 1])
+                if nk[b] == 0:
+                    assert np.all(O[h, rows] == 0) and np.all(np.isneginf(L[h, rows]))
+                    continue
+                for i in range(nq[b]):
+                    vis = [j for j in range(nk[b]) if not causal or j <= i + nk[b] - nq[b]]
+                    if not vis:
+                        assert np.all(O[h, cu_q[b] + i] == 0) and np.isneginf(L[h, cu_q[b] + i])
+                        continue
+                    kk = [k[g, cu_k[b] + j].tolist() for j in vis]
+                    vv = [v[g, cu_k[b] + j].tolist() for j in vis]
+                    Ob, Lb = brute_force([[[q[h, cu_q[b] + i].tolist()]]], [[kk]], [[vv]], 0.45, False)
+                    assert np.abs(Ob[0, 0, 0] - O[h, cu_q[b] + i]).max() <= TOL
+                    assert abs(Lb[0, 0, 0] - L[h, cu_q[b] + i]) <= TOL
+        assert np.all(O[:, -2:] == 0) and np.all(np.isnan(L[:, -2:]))
+    # changing another sequence's keys leaves sequence 2 alone
+    k2 = k.copy()
+    k2[:, cu_k[0]:cu_k[1]] += 3.0
+    O2, L2 = oracle.attention_varlen(q, k2, v, cu_q, cu_k, 0.45, True)
+    O1, L1 = oracle.attention_varlen(q, k, v, cu_q, cu_k, 0.45, True)
+    sl = slice(cu_q[2], cu_q[3])
+    assert np.array_equal(O2[:, sl], O1[:, sl]) and np.array_equal(L2[:, sl], L1[:, sl])
+    # offsets outside [0, total] are clamped: [-2, 3) reads rows [0, 3)
+    Oc, Lc = oracle.attention_varlen(q, k, v, [-2, 3, 1000], [-7, 4, 1000], 0.45, False)
+    Od, Ld = oracle.attention_varlen(q, k, v, [0, 3, tq], [0, 4, tk], 0.45, False)
+    assert np.array_equal(Oc, Od) and np.array_equal(Lc, Ld) and np.all(np.isfinite(Lc))
+
+
 ALL_PINS = [
     pin_brute_force, pin_single_key_and_causal_row0, pin_two_keys, pin_golden_fixtures,
     pin_zero_query, pin_rows_sum_to_one, pin_merge_identity, pin_shift_invariance,
     pin_permutation, pin_convex_hull, pin_causal_is_prefix, pin_gqa_is_repeated_mha,
     pin_decode_is_single_query, pin_lse_library, pin_sampled_rows_match_full,
-    pin_paged_decode_is_decode,
+    pin_paged_decode_is_decode, pin_varlen_is_per_sequence,
 ]

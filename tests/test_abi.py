@@ -29,8 +29,8 @@ def test_library_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"fa_fwd", "fa_decode", "fa_decode_paged", "fa_decode_workspace_bytes", "fa_status_string",
-            "fa_last_error"} <= set(names)
+    assert {"fa_fwd", "fa_fwd_varlen", "fa_decode", "fa_decode_paged", "fa_decode_workspace_bytes",
+            "fa_status_string", "fa_last_error"} <= set(names)
     raw = ctypes.CDLL(fa.lib_path())
     for n in names:
         assert hasattr(raw, n), f"{n} declared in fa.h but not exported"
@@ -107,6 +107,32 @@ def dec(**kw):
 ])
 def test_decode_rejects_before_launch(kw, status):
     st = dec(**kw)
+    assert st == status, (st, fa.fa_last_error())
+
+
+def fwd_varlen(**kw):
+    a = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, o=FAKE + 0x3000000, lse=None,
+             cu_q=FAKE + 0x4000000, cu_k=FAKE + 0x4100000, B=3, Hq=8, Hkv=2, total_q=1000, total_k=1200,
+             max_q=600, d=128, scale=0.088, causal=1, dtype=0, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu_q"], a["cu_k"], a["B"], a["Hq"],
+                            a["Hkv"], a["total_q"], a["total_k"], a["max_q"], a["d"], a["scale"], a["causal"],
+                            a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu_q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(cu_k=FAKE + 0x4100002), fa.FA_ERR_INVALID_ARG),
+    (dict(total_q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(max_q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(max_q=1001), fa.FA_ERR_INVALID_ARG),             # more than total_q
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(o=FAKE + 0x100), fa.FA_ERR_INVALID_ARG),          # o overlaps q
+])
+def test_fwd_varlen_rejects_before_launch(kw, status):
+    st = fwd_varlen(**kw)
     assert st == status, (st, fa.fa_last_error())
 
 

@@ -135,6 +135,16 @@ def _paged_rows_ignore_table(table_row, n, P):
     return rows // P, rows % P
 
 
+def _varlen_bounds_next(cu, b, total):
+    lo = min(max(int(cu[b]), 0), total)
+    hi = min(max(int(cu[b + 1]) + 1, lo), total)
+    return lo, hi
+
+
+def _varlen_bounds_unclamped(cu, b, total):
+    return int(cu[b]), int(cu[b + 1])
+
+
 def _scale_not_rounded(scale):
     return float(scale)
 
@@ -156,6 +166,8 @@ MUTATIONS = [
     ("scale_not_fp32", oe, "as_fp32_scale", _scale_not_rounded),
     ("paged_rows_swapped", oe, "paged_rows", _paged_rows_swapped),
     ("paged_rows_ignore_table", oe, "paged_rows", _paged_rows_ignore_table),
+    ("varlen_bounds_overrun", oe, "varlen_bounds", _varlen_bounds_next),
+    ("varlen_bounds_unclamped", oe, "varlen_bounds", _varlen_bounds_unclamped),
 ]
 
 
