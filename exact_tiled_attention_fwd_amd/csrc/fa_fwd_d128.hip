@@ -9,8 +9,9 @@
 //
 // What differs is how K and V reach LDS. The waves of one group move each
 // tile HBM -> LDS directly (global_load_lds_dwordx4: no staging registers, no
-// LDS store instructions, no vector-ALU work), into 3-slot rings issued two
-// tiles (K) and one tile (V) ahead of the step that reads them. V stays
+// LDS store instructions, no vector-ALU work), into 4-slot rings issued two
+// tiles (K) and one tile (V) ahead of the step that reads them; the fourth
+// slot lets one barrier per step order both the loads and the reuse of slots. V stays
 // row-major in LDS and is read transposed (ds_read_b64_tr_b16) as the A
 // operand of O^T += V^T P^T, so no lane shuffles are needed anywhere. The
 // vector ALUs are left to the softmax.
@@ -29,7 +30,7 @@ constexpr int kBM = kFwdBlockRows;  // 256 query rows per workgroup
 constexpr int kThreads = 512;       // 8 waves = 2 groups of 4
 constexpr int kD = 128;
 constexpr int kRows = 64;           // keys per tile
-constexpr int kSlots = 3;           // ring depth for K and for V
+constexpr int kSlots = 4;           // ring depth for K and for V
 constexpr int kTile = kRows * kD * 2;  // 16 KiB
 constexpr int KS = kD / 16;         // 8 MFMA k-steps over d
 constexpr int KB = kRows / 32;      // 2 key blocks of 32
@@ -80,7 +81,6 @@ __device__ __attribute__((always_inline)) inline void dma_barrier(int pending) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   asm volatile("s_barrier" ::: "memory");
 }
-__device__ __attribute__((always_inline)) inline void plain_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Operand reader of the layouts above. K: one 16-byte read per lane (row
 // 32 kb + lane % 32, chunk 2 ks + lane / 32). V^T: two transposed reads; lane
@@ -138,8 +138,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_d128_kernel(
     float scale_log2, int n_qt, Varlen vlen) {
   constexpr int D = kD, ROWS = kRows;
   __shared__ __attribute__((aligned(1024))) char smem[2 * kSlots * kTile];
-  char* const kring = smem;                   // K tile t in slot t % 3
-  char* const vring = smem + kSlots * kTile;  // V tile t in slot t % 3
+  char* const kring = smem;                   // K tile t in slot t % 4
+  char* const vring = smem + kSlots * kTile;  // V tile t in slot t % 4
 
   const Work wk = VARLEN ? map_work_packed(blockIdx.x, B, Hq, Hkv, n_qt) : map_work(blockIdx.x, B, Hq, Hkv, n_qt);
   const Slabs sl = slabs_of<VARLEN, D>(wk, q, k, v, o, lse, Hq, Hkv, Nq_all, Nk_all, vlen);
@@ -273,13 +273,14 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_d128_kernel(
   if (grp == 0 && 0 < n_kv) issue(false, 0);
   dma_barrier(issue_step(-1));  // K_0 has landed
 
-  // Macro-step i = phase A, barrier Y_i, phase B, barrier X_{i+1}:
-  //   group 0: A = MB(i-1), MA(i)                          B = SM(i), first reads of MB(i), MA(i+1)
+  // Step i = phase A, barrier Y_i, phase B; Y_i is the step's only barrier:
+  //   group 0: A = MB(i-1), MA(i), loads K_{i+2}, V_{i+1}   B = SM(i), first reads of MB(i), MA(i+1)
   //   group 1: A = SM(i-1), first reads of MB(i-1), MA(i)  B = MB(i-1), MA(i)
-  // Step i reads K_i and V_{i-1}, and after Y_i also K_{i+1} and V_i. The
-  // loads issued at the start of step i (K_{i+2}, V_{i+1}) go to the slots of
-  // K_{i-1} and V_{i-2}, last read in step i - 1; Y_i waits for the loads
-  // issued at step i - 1 (K_{i+1}, V_i).
+  // Y_i waits for the loads issued in step i - 1 (K_{i+1}, V_i). Between Y_i
+  // and Y_{i+1} the waves read K_i, K_{i+1}, V_{i-1} and V_i, while the loads
+  // in flight write K_{i+2}, K_{i+3}, V_{i+1} and V_{i+2}: distinct slots of
+  // the 4-slot rings. A slot is rewritten only after the barrier that follows
+  // the MFMAs consuming its last reads.
   if (grp == 0) {
     mma_pre(false, 0, 0 < wave_tiles, 0);
     for (int i = 0; i <= n_kv; ++i) {
@@ -308,7 +309,6 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_d128_kernel(
       dma_barrier(n_new);  // Y_i
       if (i < wave_tiles) softmax(i);
       mma_pre(i < wave_tiles, i, i + 1 < wave_tiles, i + 1);
-      plain_barrier();  // X_{i+1}
     }
   } else {
     for (int i = 0; i <= n_kv; ++i) {
@@ -317,7 +317,6 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_d128_kernel(
       mma_pre(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
       dma_barrier(n_new);  // Y_i
       mma(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
-      plain_barrier();  // X_{i+1}
     }
   }
 
