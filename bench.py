@@ -254,7 +254,7 @@ def cpu_cores_used():
     return cores
 
 
-def cpu_baseline_prefill(name="llama3_8b_gqa_n8192", heads=8):
+def cpu_baseline_prefill(name="llama3_8b_gqa_n8192", heads=32):
     """The oracle on `heads` full heads of the prefill workload (all query rows,
     all keys, causal): TFLOP/s by the same FLOP convention as the GPU."""
     import oracle
@@ -276,7 +276,7 @@ def cpu_baseline_prefill(name="llama3_8b_gqa_n8192", heads=8):
                       f"(float64 NumPy, score matrix materialised); {elapsed:.1f}s"}
 
 
-def cpu_baseline_varlen(name="llama3_8b_gqa_varlen", seqs=2, heads=4):
+def cpu_baseline_varlen(name="llama3_8b_gqa_varlen", seqs=16, heads=4):
     """The oracle's packed prefill on the first `seqs` sequences, `heads`
     q-heads each (all rows, causal): TFLOP/s by the GPU's FLOP convention."""
     import oracle
@@ -294,17 +294,22 @@ def cpu_baseline_varlen(name="llama3_8b_gqa_varlen", seqs=2, heads=4):
                       f"all rows, causal (float64 NumPy); {elapsed:.1f}s"}
 
 
-def cpu_baseline_decode(name="decode_32seq_gqa", seqs=32, page_size=0):
+def cpu_baseline_decode(name="decode_32seq_gqa", seqs=32, page_size=0, min_seconds=10.0):
     """The oracle's decode (paged decode when page_size > 0, through a
     shuffled page table) on the first `seqs` sequences: GB/s by the same byte
-    count as the GPU."""
+    count as the GPU. One pass takes well under a second, so each sequence's
+    call is repeated until its share (by length) of `min_seconds` is spent."""
     import oracle
     c = ai.CONFIGS[name]
     lens = ai.decode_lengths(c["seed"], c["B"], c["len_lo"], c["len_hi"])[:seqs]
     Hq, Hkv, d, dt = c["Hq"], c["Hkv"], c["d"], c["dtype"]
     elapsed = 0.0
+    nbytes = 0
+    passes = []
+    total_len = float(sum(int(n) for n in lens))
     for b in range(seqs):
         L = int(lens[b])
+        budget = min_seconds * L / total_len
         q = np.stack([ai.bits_to_f64(ai.slab(c["seed"], ai.Q_ID, b, h, 1, d, dt), dt)[0] for h in range(Hq)])[None]
         kc = np.stack([ai.bits_to_f64(ai.slab(c["seed"], ai.K_ID, b, g, L, d, dt), dt) for g in range(Hkv)])[None]
         vc = np.stack([ai.bits_to_f64(ai.slab(c["seed"], ai.V_ID, b, g, L, d, dt), dt) for g in range(Hkv)])[None]
@@ -318,16 +323,22 @@ def cpu_baseline_decode(name="decode_32seq_gqa", seqs=32, page_size=0):
             vp = np.empty((n_pg, Hkv, page_size, d))
             kp[order] = kpad[0].reshape(Hkv, n_pg, page_size, d).transpose(1, 0, 2, 3)
             vp[order] = vpad[0].reshape(Hkv, n_pg, page_size, d).transpose(1, 0, 2, 3)
-            t0 = time.perf_counter()
-            oracle.decode_paged(q, kp, vp, order[None, :], [L], 1.0 / math.sqrt(d))
+            call = lambda: oracle.decode_paged(q, kp, vp, order[None, :], [L], 1.0 / math.sqrt(d))
         else:
+            call = lambda: oracle.decode(q, kc, vc, [L], 1.0 / math.sqrt(d))
+        spent, n = 0.0, 0
+        while n == 0 or spent < budget:
             t0 = time.perf_counter()
-            oracle.decode(q, kc, vc, [L], 1.0 / math.sqrt(d))
-        elapsed += time.perf_counter() - t0
-    nbytes = decode_bytes(lens, Hq, Hkv, d)
+            call()
+            spent += time.perf_counter() - t0
+            n += 1
+        elapsed += spent
+        nbytes += n * decode_bytes([L], Hq, Hkv, d)
+        passes.append(n)
     what = f"paged ({page_size}-row pages), " if page_size else ""
     return {"value": nbytes / elapsed / 1e9, "unit": "GB/s", "cores": cpu_cores_used(), "kind": "oracle",
-            "sample": f"{what}first {seqs} of 32 sequences (lengths {lens.tolist()}), all 32 q-heads; {elapsed:.1f}s"}
+            "sample": f"{what}first {seqs} of 32 sequences (lengths {lens.tolist()}), all 32 q-heads, each sequence "
+                      f"repeated {min(passes)}-{max(passes)} times; {elapsed:.1f}s"}
 
 
 # ------------------------------------------------------------------ modes
