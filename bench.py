@@ -109,7 +109,11 @@ def to_dev(bits, dtype):
 
 
 class Prefill:
-    def __init__(self, fa, name, causal):
+    """One prefill layer; layout "bhnd" holds q, k, v, o as [B, H, N, d],
+    "bshd" as (batch, seq, heads, dim) tensors read and written in place
+    through their strides."""
+
+    def __init__(self, fa, name, causal, layout="bhnd"):
         import torch
         c = ai.CONFIGS[name]
         self.fa, self.name, self.causal = fa, name, causal
@@ -119,6 +123,10 @@ class Prefill:
         self.q, self.k, self.v = to_dev(x["q"], self.dtype), to_dev(x["k"], self.dtype), to_dev(x["v"], self.dtype)
         del x
         self.o = torch.empty_like(self.q)
+        if layout == "bshd":
+            # the (B, N, H, d) storage, seen as [B, H, N, d] views
+            self.q, self.k, self.v, self.o = (t.transpose(1, 2).contiguous().transpose(1, 2)
+                                              for t in (self.q, self.k, self.v, self.o))
         self.lse = torch.empty((self.B, self.Hq, self.N), dtype=torch.float32, device="cuda")
         self.flops = prefill_flops(self.B, self.Hq, self.N, self.N, self.d, causal)
         self.bytes = prefill_bytes(self.B, self.Hq, self.Hkv, self.N, self.N, self.d)
@@ -384,18 +392,19 @@ def main():
 
     cfg = args.config
     run_prefill = cfg in ("default", "tiny_mha_n128", "mha_n4096_fp16", "mha_n4096_fp16_causal", "llama3_8b_gqa_n8192",
-                          "llama3_8b_gqa_n131072", "llama3_8b_gqa_varlen")
+                          "llama3_8b_gqa_n131072", "llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd")
     run_decode = cfg in ("default", "decode_32seq_gqa", "decode_32seq_gqa_paged")
     paged = cfg == "decode_32seq_gqa_paged"
     if not (run_prefill or run_decode):
         raise SystemExit(f"unknown --config {cfg}")
-    pname = "llama3_8b_gqa_n8192" if cfg == "default" else cfg.replace("_causal", "")
+    pname = "llama3_8b_gqa_n8192" if cfg in ("default", "llama3_8b_gqa_n8192_bshd") else cfg.replace("_causal", "")
     causal = cfg in ("default", "llama3_8b_gqa_n8192", "llama3_8b_gqa_n131072", "mha_n4096_fp16_causal",
-                     "llama3_8b_gqa_varlen")
+                     "llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd")
     parts = []
     pre = dec = None
     if run_prefill:
-        pre = PrefillVarlen(fa) if cfg == "llama3_8b_gqa_varlen" else Prefill(fa, pname, causal)
+        pre = (PrefillVarlen(fa) if cfg == "llama3_8b_gqa_varlen"
+               else Prefill(fa, pname, causal, layout="bshd" if cfg.endswith("_bshd") else "bhnd"))
         parts.append(pre)
     if run_decode:
         dec = DecodePaged(fa, num_splits=args.num_splits) if paged else Decode(fa, num_splits=args.num_splits)
@@ -409,10 +418,12 @@ def main():
         t_ms = float(np.mean(per[i]))
         tflops = pre.flops / (t_ms * 1e-3) / 1e12
         out.update(value=round(tflops, 2), unit="TFLOP/s")
-        out["prefill"] = {"workload": f"{pname} causal={causal}", "ms_mean": round(t_ms, 4),
+        wl = cfg if cfg in ("llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd") else pname
+        out["prefill"] = {"workload": f"{wl} causal={causal}", "ms_mean": round(t_ms, 4),
                           "ms_min": round(float(np.min(per[i])), 4), "tflops": round(tflops, 2),
                           "frac_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS, 4)}
-        traffic = counter_traffic(f"fa_fwd_{pname}_counters.md") if causal else None
+        prof = cfg if cfg in ("llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd") else pname
+        traffic = counter_traffic(f"fa_fwd_{prof}_counters.md") if causal else None
         out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
                            "algorithmic_bytes": pre.bytes, "flops_per_launch": pre.flops}

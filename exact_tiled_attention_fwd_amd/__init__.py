@@ -6,12 +6,20 @@ runs in the HIP kernels of that library; this module only marshals arguments.
 PyTorch supplies device memory and the current stream.
 
 Raw entry points, same names and argument order as the C header:
-    fa_fwd, fa_fwd_varlen, fa_decode, fa_decode_paged, fa_decode_workspace_bytes,
-    fa_status_string, fa_last_error, fa_abi_version
+    fa_fwd, fa_fwd_strided, fa_fwd_varlen, fa_fwd_varlen_strided, fa_decode,
+    fa_decode_paged, fa_decode_workspace_bytes, fa_status_string,
+    fa_last_error, fa_abi_version
 Tensor-level helpers:
     attention(q, k, v, causal=False, scale=None) -> (o, lse)
+        q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d], any strides with a unit last one
     attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                      causal=False, scale=None) -> (o, lse)
+        q [Hq,total_q,d], k/v [Hkv,total_k,d], any strides likewise
+    flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False)
+        -> o, for q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d]
+    flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                           max_seqlen_k, dropout_p=0.0, softmax_scale=None,
+                           causal=False) -> o, for q [total_q,Hq,d]
     decode(q, k_cache, v_cache, seqlens, scale=None, num_splits=0) -> (o, lse)
     decode_paged(q, k_pages, v_pages, block_table, seqlens, scale=None,
                  num_splits=0) -> (o, lse)
@@ -30,8 +38,9 @@ import torch  # loads the HIP runtime that libfa.so then binds to
 __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
     "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FAError", "lib_path", "load_library",
-    "fa_fwd", "fa_fwd_varlen", "fa_decode", "fa_decode_paged", "fa_decode_workspace_bytes", "fa_status_string",
-    "fa_last_error", "fa_abi_version", "attention", "attention_varlen", "decode", "decode_paged", "dtype_code",
+    "fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_varlen_strided", "fa_decode", "fa_decode_paged",
+    "fa_decode_workspace_bytes", "fa_status_string", "fa_last_error", "fa_abi_version", "attention",
+    "attention_varlen", "flash_attn_func", "flash_attn_varlen_func", "decode", "decode_paged", "dtype_code",
 ]
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
@@ -77,6 +86,10 @@ def load_library():
     lib.fa_fwd.restype = i
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_varlen.restype = i
+    lib.fa_fwd_strided.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_strided.restype = i
+    lib.fa_fwd_varlen_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_fwd_varlen_strided.restype = i
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
     lib.fa_decode.restype = i
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, i, i, vp]
@@ -116,6 +129,33 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total
     """Call the C ``fa_fwd_varlen`` with integer device addresses; returns the status."""
     return load_library().fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q, total_k,
                                         max_seqlen_q, d, scale, causal, dtype, stream)
+
+
+def _i64_array(strides):
+    arr = (ctypes.c_int64 * len(strides))(*[int(x) for x in strides])
+    return arr
+
+
+def fa_fwd_strided(q, k, v, o, lse, strides, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, stream) -> int:
+    """Call the C ``fa_fwd_strided``; `strides` is a sequence of 12 ints
+    (batch, head, row strides of q, k, v, o in elements)."""
+    if len(strides) != 12:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "fa_fwd_strided needs 12 strides")
+    arr = _i64_array(strides)
+    return load_library().fa_fwd_strided(q, k, v, o, lse, ctypes.cast(arr, ctypes.c_void_p), B, Hq, Hkv, Nq, Nk, d,
+                                         scale, causal, dtype, stream)
+
+
+def fa_fwd_varlen_strided(q, k, v, o, lse, strides, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q, total_k,
+                          max_seqlen_q, d, scale, causal, dtype, stream) -> int:
+    """Call the C ``fa_fwd_varlen_strided``; `strides` is a sequence of 8 ints
+    (head, token strides of q, k, v, o in elements)."""
+    if len(strides) != 8:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "fa_fwd_varlen_strided needs 8 strides")
+    arr = _i64_array(strides)
+    return load_library().fa_fwd_varlen_strided(q, k, v, o, lse, ctypes.cast(arr, ctypes.c_void_p), cu_seqlens_q,
+                                                cu_seqlens_k, B, Hq, Hkv, total_q, total_k, max_seqlen_q, d, scale,
+                                                causal, dtype, stream)
 
 
 def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, workspace_bytes,
@@ -162,14 +202,17 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _check_tensor(name, t, ndim, device=None):
+def _check_tensor(name, t, ndim, device=None, strided=False):
     if not isinstance(t, torch.Tensor):
         raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must be a torch.Tensor")
     if t.dim() != ndim:
         raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must have {ndim} dims, got {tuple(t.shape)}")
     if not t.is_cuda:
         raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must be on the GPU")
-    if not t.is_contiguous():
+    if strided:
+        if t.stride(-1) != 1 and t.shape[-1] > 1:
+            raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must have a unit stride in its last dim")
+    elif not t.is_contiguous():
         raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must be contiguous")
     if device is not None and t.device != device:
         raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} is on {t.device}, expected {device}")
@@ -180,11 +223,14 @@ def _stream(device):
 
 
 def attention(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
-    """O, LSE for q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] (bf16/fp16, contiguous, same GPU)."""
-    _check_tensor("q", q, 4)
+    """O, LSE for q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] (bf16/fp16, same GPU). Any
+    strides with a unit last one are accepted (e.g. transposed views of
+    (batch, seq, heads, dim) tensors); contiguous tensors go through fa_fwd,
+    others through fa_fwd_strided."""
+    _check_tensor("q", q, 4, strided=True)
     dev = q.device
-    _check_tensor("k", k, 4, dev)
-    _check_tensor("v", v, 4, dev)
+    _check_tensor("k", k, 4, dev, strided=True)
+    _check_tensor("v", v, 4, dev, strided=True)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise FAInvalidArgument(FA_ERR_INVALID_ARG, "q, k and v must share a dtype")
     B, Hq, Nq, d = q.shape
@@ -195,11 +241,20 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _check_tensor("out", out, 4, dev, strided=True)
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "out must match q in shape and dtype")
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    _check_tensor("lse", lse, 3, dev)
     with torch.cuda.device(dev):
-        st = fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
-                    float(scale), int(bool(causal)), dtype_code(q.dtype), _stream(dev))
+        if all(t.is_contiguous() for t in (q, k, v, out)):
+            st = fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                        float(scale), int(bool(causal)), dtype_code(q.dtype), _stream(dev))
+        else:
+            strides = [*q.stride()[:3], *k.stride()[:3], *v.stride()[:3], *out.stride()[:3]]
+            st = fa_fwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), strides, B, Hq, Hkv, Nq, Nk, d,
+                                float(scale), int(bool(causal)), dtype_code(q.dtype), _stream(dev))
     _raise_for(st)
     return out, lse
 
@@ -207,11 +262,13 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = False,
                      scale: float | None = None, out=None, lse=None):
     """Packed variable-length batch: q [Hq,total_q,d], k/v [Hkv,total_k,d],
-    cu_seqlens_* int32 [B+1] on the device, max_seqlen_q a host int."""
-    _check_tensor("q", q, 3)
+    cu_seqlens_* int32 [B+1] on the device, max_seqlen_q a host int. Any
+    strides with a unit last one are accepted (e.g. transposed views of
+    (total, heads, dim) tensors)."""
+    _check_tensor("q", q, 3, strided=True)
     dev = q.device
-    _check_tensor("k", k, 3, dev)
-    _check_tensor("v", v, 3, dev)
+    _check_tensor("k", k, 3, dev, strided=True)
+    _check_tensor("v", v, 3, dev, strided=True)
     _check_tensor("cu_seqlens_q", cu_seqlens_q, 1, dev)
     _check_tensor("cu_seqlens_k", cu_seqlens_k, 1, dev)
     if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
@@ -227,14 +284,61 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, cau
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _check_tensor("out", out, 3, dev, strided=True)
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "out must match q in shape and dtype")
     if lse is None:
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    _check_tensor("lse", lse, 2, dev)
     with torch.cuda.device(dev):
-        st = fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
-                           B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), d, float(scale), int(bool(causal)),
-                           dtype_code(q.dtype), _stream(dev))
+        if all(t.is_contiguous() for t in (q, k, v, out)):
+            st = fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                               _ptr(cu_seqlens_k), B, Hq, Hkv, total_q, total_k, int(max_seqlen_q), d, float(scale),
+                               int(bool(causal)), dtype_code(q.dtype), _stream(dev))
+        else:
+            strides = [*q.stride()[:2], *k.stride()[:2], *v.stride()[:2], *out.stride()[:2]]
+            st = fa_fwd_varlen_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), strides,
+                                       _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, Hq, Hkv, total_q, total_k,
+                                       int(max_seqlen_q), d, float(scale), int(bool(causal)), dtype_code(q.dtype),
+                                       _stream(dev))
     _raise_for(st)
     return out, lse
+
+
+def _no_dropout(dropout_p):
+    if dropout_p:
+        raise FAUnsupported(FA_ERR_UNSUPPORTED, "dropout is not supported (forward inference path only)")
+
+
+def flash_attn_func(q, k, v, dropout_p: float = 0.0, softmax_scale: float | None = None, causal: bool = False,
+                    return_lse: bool = False):
+    """The flash_attn_func calling convention: q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d]
+    (batch, seq, heads, dim); returns o [B,Nq,Hq,d] in the same layout (and
+    the LSE [B,Hq,Nq] fp32 with return_lse). No copies: the kernels read and
+    write the (batch, seq, heads, dim) tensors through their strides."""
+    _no_dropout(dropout_p)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, 4, strided=True)
+    out = torch.empty_like(q)
+    o, lse = attention(q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2), causal=causal,
+                       scale=softmax_scale, out=out.transpose(1, 2))
+    return (out, lse) if return_lse else out
+
+
+def flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                           dropout_p: float = 0.0, softmax_scale: float | None = None, causal: bool = False,
+                           return_lse: bool = False):
+    """The flash_attn_varlen_func calling convention: q [total_q,Hq,d],
+    k/v [total_k,Hkv,d] (packed tokens, heads, dim), cu_seqlens_* int32 [B+1];
+    returns o [total_q,Hq,d] (and the LSE [Hq,total_q] fp32 with return_lse).
+    max_seqlen_k is accepted for the signature and not needed."""
+    _no_dropout(dropout_p)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, 3, strided=True)
+    out = torch.empty_like(q)
+    o, lse = attention_varlen(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1), cu_seqlens_q, cu_seqlens_k,
+                              max_seqlen_q, causal=causal, scale=softmax_scale, out=out.transpose(0, 1))
+    return (out, lse) if return_lse else out
 
 
 def decode(q, k_cache, v_cache, seqlens, scale: float | None = None, num_splits: int = 0,

@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -102,6 +103,110 @@ fa::DecodePlan make_plan(int B, int Hkv, int Lcap, int num_splits, int Hq, int d
   return p;
 }
 
+// Element strides of one tensor dimension.
+struct Dim {
+  long long size, stride;
+};
+
+// Largest element offset any index reaches (strides >= 0), or -1 on overflow
+// past 2^61.
+long long max_offset(std::initializer_list<Dim> dims, int d) {
+  __int128 acc = d - 1;
+  for (const Dim& x : dims) acc += (__int128)(x.size - 1) * x.stride;
+  return acc > ((__int128)1 << 61) ? -1 : (long long)acc;
+}
+
+// No two indices of the tensor share an element: with the dimensions of more
+// than one index sorted by stride, each stride exceeds the largest offset the
+// smaller ones reach (the head-dim has stride 1 and d entries).
+bool rows_disjoint(std::initializer_list<Dim> dims, int d) {
+  Dim ds[4];
+  int n = 0;
+  ds[n++] = Dim{d, 1};
+  for (const Dim& x : dims)
+    if (x.size > 1) ds[n++] = x;
+  std::sort(ds, ds + n, [](const Dim& a, const Dim& b) { return a.stride < b.stride; });
+  __int128 reach = 0;
+  for (int i = 0; i < n; ++i) {
+    if ((__int128)ds[i].stride <= reach) return false;
+    reach += (__int128)(ds[i].size - 1) * ds[i].stride;
+  }
+  return true;
+}
+
+// Shared by fa_fwd, fa_fwd_strided, fa_fwd_varlen and fa_fwd_varlen_strided.
+// cu_q != nullptr selects the packed layout (Nq, Nk unused; batch strides
+// ignored).
+fa_status fwd_impl(const char* fn, const void* q, const void* k, const void* v, void* o, float* lse,
+                   const fa::Layout& ly, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   int dtype, void* stream, const int32_t* cu_q, const int32_t* cu_k, int total_q, int total_k,
+                   int max_seqlen_q) {
+  const bool packed = cu_q != nullptr || cu_k != nullptr;
+  if (!q || !k || !v || !o) return fail(FA_ERR_INVALID_ARG, "%s: q, k, v and o must be non-null", fn);
+  if (packed && (!cu_q || !cu_k))
+    return fail(FA_ERR_INVALID_ARG, "%s: cu_seqlens_q and cu_seqlens_k must be non-null", fn);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(FA_ERR_INVALID_ARG, "%s: q, k, v and o must be 16-byte aligned", fn);
+  if (packed && (!aligned(cu_q, 4) || !aligned(cu_k, 4)))
+    return fail(FA_ERR_INVALID_ARG, "%s: cu_seqlens_q and cu_seqlens_k must be 4-byte aligned", fn);
+  if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "%s: lse must be 4-byte aligned", fn);
+  if (packed) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || total_q <= 0 || total_k <= 0 || max_seqlen_q <= 0 || d <= 0)
+      return fail(FA_ERR_INVALID_ARG,
+                  "%s: sizes must be positive (B=%d Hq=%d Hkv=%d total_q=%d total_k=%d max_seqlen_q=%d d=%d)", fn, B,
+                  Hq, Hkv, total_q, total_k, max_seqlen_q, d);
+    if (max_seqlen_q > total_q)
+      return fail(FA_ERR_INVALID_ARG, "%s: max_seqlen_q=%d exceeds total_q=%d", fn, max_seqlen_q, total_q);
+  } else if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) {
+    return fail(FA_ERR_INVALID_ARG, "%s: sizes must be positive (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d)", fn, B, Hq, Hkv,
+                Nq, Nk, d);
+  }
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "%s: causal must be 0 or 1", fn);
+  fa_status st = check_common(d, dtype, scale, Hq, Hkv);
+  if (st != FA_OK) return st;
+  if (!packed && causal && Nq > Nk)
+    return fail(FA_ERR_INVALID_ARG, "%s: causal attention needs Nq <= Nk (Nq=%d Nk=%d)", fn, Nq, Nk);
+  // Strides: non-negative multiples of 8 elements (16-byte rows); row strides
+  // below 2^24 elements (32-bit offsets within a key tile), others below 2^40.
+  const long long* all[4] = {ly.q, ly.k, ly.v, ly.o};
+  const char* names[4] = {"q", "k", "v", "o"};
+  for (int t = 0; t < 4; ++t)
+    for (int i = packed ? 1 : 0; i < 3; ++i) {
+      const long long x = all[t][i];
+      if (x < 0 || (x & 7) || x >= (i == 2 ? (1LL << 24) : (1LL << 40)))
+        return fail(FA_ERR_INVALID_ARG,
+                    "%s: stride %d of %s is %lld; strides must be non-negative multiples of 8 elements, row strides "
+                    "below 2^24 and the others below 2^40",
+                    fn, i, names[t], x);
+    }
+  const long long bq = packed ? 1 : B, rq = packed ? total_q : Nq, rk = packed ? total_k : Nk;
+  const long long oq = max_offset({{bq, ly.q[0]}, {Hq, ly.q[1]}, {rq, ly.q[2]}}, d);
+  const long long ok = max_offset({{bq, ly.k[0]}, {Hkv, ly.k[1]}, {rk, ly.k[2]}}, d);
+  const long long ov = max_offset({{bq, ly.v[0]}, {Hkv, ly.v[1]}, {rk, ly.v[2]}}, d);
+  const long long oo = max_offset({{bq, ly.o[0]}, {Hq, ly.o[1]}, {rq, ly.o[2]}}, d);
+  size_t lb;
+  if (oq < 0 || ok < 0 || ov < 0 || oo < 0 || !mul_bytes(lb, {bq, Hq, rq, 4}))
+    return fail(FA_ERR_INVALID_ARG, "%s: tensor sizes overflow", fn);
+  if (!rows_disjoint({{bq, ly.o[0]}, {Hq, ly.o[1]}, {rq, ly.o[2]}}, d))
+    return fail(FA_ERR_INVALID_ARG, "%s: the strides of o make two of its elements share memory", fn);
+  const int rows = packed ? max_seqlen_q : Nq;
+  if ((long long)((rows + fa::kFwdBlockRows - 1) / fa::kFwdBlockRows) * B * Hq > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "%s: grid too large", fn);
+  const size_t qb = 2 * (size_t)(oq + 1), kb = 2 * (size_t)(ok + 1), vb = 2 * (size_t)(ov + 1),
+               obb = 2 * (size_t)(oo + 1);
+  if (overlap(o, obb, q, qb) || overlap(o, obb, k, kb) || overlap(o, obb, v, vb))
+    return fail(FA_ERR_INVALID_ARG, "%s: o overlaps an input", fn);
+  if (lse && (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, vb) || overlap(lse, lb, o, obb)))
+    return fail(FA_ERR_INVALID_ARG, "%s: lse overlaps another tensor", fn);
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, cu_q, cu_k, total_q, total_k,
+                max_seqlen_q, ly};
+  hipError_t e = fa::launch_fwd(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -123,68 +228,49 @@ const char* fa_last_error(void) { return g_last_error.c_str(); }
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
                  int Nk, int d, float scale, int causal, int dtype, void* stream) {
   g_last_error.clear();
-  if (!q || !k || !v || !o) return fail(FA_ERR_INVALID_ARG, "q, k, v and o must be non-null");
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
-    return fail(FA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
-  if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0)
-    return fail(FA_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d)", B, Hq, Hkv, Nq, Nk, d);
-  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
-  fa_status st = check_common(d, dtype, scale, Hq, Hkv);
-  if (st != FA_OK) return st;
-  if (causal && Nq > Nk) return fail(FA_ERR_INVALID_ARG, "causal attention needs Nq <= Nk (Nq=%d Nk=%d)", Nq, Nk);
-  size_t qb, kb, lb;
-  if (!mul_bytes(qb, {B, Hq, Nq, d, 2}) || !mul_bytes(kb, {B, Hkv, Nk, d, 2}) || !mul_bytes(lb, {B, Hq, Nq, 4}))
-    return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
-  if ((long long)((Nq + fa::kFwdBlockRows - 1) / fa::kFwdBlockRows) * B * Hq > 0x7fffffffLL)
-    return fail(FA_ERR_UNSUPPORTED, "grid too large");
-  if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb))
-    return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
-  if (lse && (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) || overlap(lse, lb, o, qb)))
-    return fail(FA_ERR_INVALID_ARG, "lse overlaps another tensor");
-  st = check_device();
-  if (st != FA_OK) return st;
-  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, nullptr, nullptr, 0, 0, 0};
-  hipError_t e = fa::launch_fwd(a, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd launch: %s", hipGetErrorString(e));
-  return FA_OK;
+  const long long qh = (long long)Nq * d, kh = (long long)Nk * d;
+  const fa::Layout ly{{(long long)Hq * qh, qh, d}, {(long long)Hkv * kh, kh, d}, {(long long)Hkv * kh, kh, d},
+                      {(long long)Hq * qh, qh, d}};
+  return fwd_impl("fa_fwd", q, k, v, o, lse, ly, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, stream, nullptr,
+                  nullptr, 0, 0, 0);
+}
+
+fa_status fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse, const int64_t* strides,
+                         int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                         void* stream) {
+  g_last_error.clear();
+  if (!strides) return fail(FA_ERR_INVALID_ARG, "fa_fwd_strided: strides must be non-null");
+  fa::Layout ly;
+  for (int i = 0; i < 3; ++i) {
+    ly.q[i] = strides[i];
+    ly.k[i] = strides[3 + i];
+    ly.v[i] = strides[6 + i];
+    ly.o[i] = strides[9 + i];
+  }
+  return fwd_impl("fa_fwd_strided", q, k, v, o, lse, ly, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, stream, nullptr,
+                  nullptr, 0, 0, 0);
 }
 
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens_q,
                          const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int total_q, int total_k,
                          int max_seqlen_q, int d, float scale, int causal, int dtype, void* stream) {
   g_last_error.clear();
-  if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k)
-    return fail(FA_ERR_INVALID_ARG, "q, k, v, o, cu_seqlens_q and cu_seqlens_k must be non-null");
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
-    return fail(FA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned");
-  if (!aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
-    return fail(FA_ERR_INVALID_ARG, "cu_seqlens_q and cu_seqlens_k must be 4-byte aligned");
-  if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || total_q <= 0 || total_k <= 0 || max_seqlen_q <= 0 || d <= 0)
-    return fail(FA_ERR_INVALID_ARG,
-                "sizes must be positive (B=%d Hq=%d Hkv=%d total_q=%d total_k=%d max_seqlen_q=%d d=%d)", B, Hq, Hkv,
-                total_q, total_k, max_seqlen_q, d);
-  if (max_seqlen_q > total_q) return fail(FA_ERR_INVALID_ARG, "max_seqlen_q=%d exceeds total_q=%d", max_seqlen_q, total_q);
-  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "causal must be 0 or 1");
-  fa_status st = check_common(d, dtype, scale, Hq, Hkv);
-  if (st != FA_OK) return st;
-  size_t qb, kb, lb;
-  if (!mul_bytes(qb, {Hq, total_q, d, 2}) || !mul_bytes(kb, {Hkv, total_k, d, 2}) || !mul_bytes(lb, {Hq, total_q, 4}))
-    return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
-  if ((long long)((max_seqlen_q + fa::kFwdBlockRows - 1) / fa::kFwdBlockRows) * B * Hq > 0x7fffffffLL)
-    return fail(FA_ERR_UNSUPPORTED, "grid too large");
-  if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb))
-    return fail(FA_ERR_INVALID_ARG, "o overlaps an input");
-  if (lse && (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) || overlap(lse, lb, o, qb)))
-    return fail(FA_ERR_INVALID_ARG, "lse overlaps another tensor");
-  st = check_device();
-  if (st != FA_OK) return st;
-  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, 0, 0, d, scale, causal, dtype,
-                cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q};
-  hipError_t e = fa::launch_fwd(a, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd_varlen launch: %s", hipGetErrorString(e));
-  return FA_OK;
+  const long long qh = (long long)total_q * d, kh = (long long)total_k * d;
+  const fa::Layout ly{{0, qh, d}, {0, kh, d}, {0, kh, d}, {0, qh, d}};
+  return fwd_impl("fa_fwd_varlen", q, k, v, o, lse, ly, B, Hq, Hkv, 0, 0, d, scale, causal, dtype, stream,
+                  cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q);
+}
+
+fa_status fa_fwd_varlen_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int64_t* strides, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                int B, int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q, int d,
+                                float scale, int causal, int dtype, void* stream) {
+  g_last_error.clear();
+  if (!strides) return fail(FA_ERR_INVALID_ARG, "fa_fwd_varlen_strided: strides must be non-null");
+  const fa::Layout ly{{0, strides[0], strides[1]}, {0, strides[2], strides[3]}, {0, strides[4], strides[5]},
+                      {0, strides[6], strides[7]}};
+  return fwd_impl("fa_fwd_varlen_strided", q, k, v, o, lse, ly, B, Hq, Hkv, 0, 0, d, scale, causal, dtype, stream,
+                  cu_seqlens_q, cu_seqlens_k, total_q, total_k, max_seqlen_q);
 }
 
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Lcap, int d, int num_splits) {

@@ -31,7 +31,7 @@ template <int DT, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Nq_all, int Nk_all,
-    float scale_log2, int n_qt, Varlen vlen) {
+    float scale_log2, int n_qt, Varlen vlen, Layout ly) {
   constexpr int ROWS = 8192 / D;  // keys per tile: 64 (d=128) or 128 (d=64)
   using T = Tile<D, ROWS>;
   __shared__ __attribute__((aligned(16))) char smem[2 * T::K_BYTES + 2 * T::VT_BYTES];
@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
   char* const vring = smem + 2 * T::K_BYTES;   // V^T tiles, slot = tile & 1
 
   const Work wk = VARLEN ? map_work_packed(blockIdx.x, B, Hq, Hkv, n_qt) : map_work(blockIdx.x, B, Hq, Hkv, n_qt);
-  const Slabs sl = slabs_of<VARLEN, D>(wk, q, k, v, o, lse, Hq, Hkv, Nq_all, Nk_all, vlen);
+  const Slabs sl = slabs_of<VARLEN>(wk, q, k, v, o, lse, Hq, Nq_all, Nk_all, vlen, ly);
   const int Nq = sl.Nq, Nk = sl.Nk;
   const int q0 = wk.qt * kBM;
   if (VARLEN && q0 >= Nq) return;  // past this sequence's rows (the whole workgroup)
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
 #pragma unroll
   for (int ks = 0; ks < T::KS; ++ks) {
     if (qrow < Nq)
-      qop[ks] = *reinterpret_cast<const u32x4*>(qp + (size_t)qrow * D + 16 * ks + 8 * half);
+      qop[ks] = *reinterpret_cast<const u32x4*>(qp + (size_t)qrow * sl.qs + 16 * ks + 8 * half);
     else
       qop[ks] = u32x4{0u, 0u, 0u, 0u};
   }
@@ -135,15 +135,15 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
   // barrier that ends the last phase reading its previous tile.
   if (grp == 0) {
     u32x4 rv[T::U][4];
-    load_v<D, ROWS>(vp, tile_rows(0), gtid, rv);
+    load_v<D, ROWS>(vp, sl.vs, tile_rows(0), gtid, rv);
     store_v<D, ROWS>(vring, gtid, rv);
-    if (n_kv > 1) load_v<D, ROWS>(vp + (size_t)ROWS * D, tile_rows(1), gtid, rv);
+    if (n_kv > 1) load_v<D, ROWS>(vp + (size_t)ROWS * sl.vs, sl.vs, tile_rows(1), gtid, rv);
     __syncthreads();
     mma_pre(false, -1, 0 < wave_tiles, 0);
     for (int i = 0; i <= n_kv; ++i) {
       if (i >= 1 && i < n_kv) {
         store_v<D, ROWS>(vring + (i & 1) * T::VT_BYTES, gtid, rv);
-        if (i + 1 < n_kv) load_v<D, ROWS>(vp + (size_t)(i + 1) * ROWS * D, tile_rows(i + 1), gtid, rv);
+        if (i + 1 < n_kv) load_v<D, ROWS>(vp + (size_t)(i + 1) * ROWS * sl.vs, sl.vs, tile_rows(i + 1), gtid, rv);
       }
       mma(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
       __syncthreads();
@@ -154,11 +154,11 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
     }
   } else {
     u32x4 rk[TileRegs<D, ROWS>::KU];
-    load_k<D, ROWS>(kp, tile_rows(0), gtid, rk);
+    load_k<D, ROWS>(kp, sl.ks, tile_rows(0), gtid, rk);
     store_k<D, ROWS>(kring, gtid, rk);
     __syncthreads();
     for (int i = 0; i <= n_kv; ++i) {
-      if (i + 1 < n_kv) load_k<D, ROWS>(kp + (size_t)(i + 1) * ROWS * D, tile_rows(i + 1), gtid, rk);
+      if (i + 1 < n_kv) load_k<D, ROWS>(kp + (size_t)(i + 1) * ROWS * sl.ks, sl.ks, tile_rows(i + 1), gtid, rk);
       if (i >= 1 && i - 1 < wave_tiles) softmax(i - 1);
       // V_{i-1} and K_i were completed before the last barrier.
       mma_pre(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
   const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < Nq) {
-    uint16_t* orow = sl.o + (size_t)qrow * D;
+    uint16_t* orow = sl.o + (size_t)qrow * sl.os;
 #pragma unroll
     for (int mt = 0; mt < T::MT; ++mt)
 #pragma unroll
@@ -199,7 +199,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const Varlen vl{a.cu_q, a.cu_k, a.total_q, a.total_k};
   hipLaunchKernelGGL((fa_fwd_kernel<DT, D, CAUSAL, VARLEN>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_qt, vl);
+                     a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_qt, vl, a.layout);
   return hipGetLastError();
 }
 

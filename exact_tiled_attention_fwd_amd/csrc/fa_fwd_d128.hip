@@ -44,20 +44,20 @@ constexpr int MT = kD / 32;         // 4 row blocks of O^T
 __device__ inline int k_phys(int row, int c) { return c ^ (row & 15); }
 __device__ inline int v_phys(int row, int c) { return c ^ (4 * (row & 3)); }
 
-// Byte offset in the global tile of the 16-byte chunk that load instruction
-// i (0..3) of wave w (0..3 of the loading group) writes to LDS position
-// p = 256 i + 64 w + lane (row p / 16, position p % 16). The swizzles are
-// involutions, so position -> chunk uses the same map. Rows at or beyond
-// nvalid re-read row nvalid - 1: their scores are masked to -inf and
-// contribute exactly 0. For a full tile the offset of instruction i is that
-// of instruction 0 plus 4096 i (the swizzles depend on the row only through
-// row % 16), so one offset register serves all four.
+// Byte offset in the global tile (rows rsb bytes apart) of the 16-byte chunk
+// that load instruction i (0..3) of wave w (0..3 of the loading group)
+// writes to LDS position p = 256 i + 64 w + lane (row p / 16, position
+// p % 16). The swizzles are involutions, so position -> chunk uses the same
+// map. Rows at or beyond nvalid re-read row nvalid - 1: their scores are
+// masked to -inf and contribute exactly 0. For a full tile the offset of
+// instruction i is that of instruction 0 plus 16 i rows (the swizzles depend
+// on the row only through row % 16), so one offset register serves all four.
 template <bool IS_V>
-__device__ inline uint32_t dma_src(int i, int w, int lane, int nvalid) {
+__device__ inline uint32_t dma_src(int i, int w, int lane, int nvalid, uint32_t rsb) {
   const int p = 256 * i + 64 * w + lane;
   const int row = p >> 4, pos = p & 15;
   const int c = IS_V ? v_phys(row, pos) : k_phys(row, pos);
-  return (uint32_t)(min(row, nvalid - 1) * (kD * 2) + c * 16);
+  return (uint32_t)min(row, nvalid - 1) * rsb + (uint32_t)(c * 16);
 }
 
 // One 1 KiB direct-to-LDS load: lane l's 16 bytes from sbase + voff land at
@@ -120,13 +120,14 @@ struct DmaSpread {
   uint32_t kslot, vslot;
   bool has_k, has_v;
   uint32_t dk, dv;
+  long long kstep, vstep;  // 16 rows, in elements
   __device__ __attribute__((always_inline)) void operator()(int t) const {
     if ((t & 3) != 2) return;
     const int j = t >> 2;
     if (j < 4) {
-      if (has_k) dma16(kbase + 2048 * j, dk, kslot + 4096 * j);
+      if (has_k) dma16(kbase + kstep * j, dk, kslot + 4096 * j);
     } else {
-      if (has_v) dma16(vbase + 2048 * (j - 4), dv, vslot + 4096 * (j - 4));
+      if (has_v) dma16(vbase + vstep * (j - 4), dv, vslot + 4096 * (j - 4));
     }
   }
 };
@@ -135,14 +136,14 @@ template <int DT, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_d128_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Nq_all, int Nk_all,
-    float scale_log2, int n_qt, Varlen vlen) {
+    float scale_log2, int n_qt, Varlen vlen, Layout ly) {
   constexpr int D = kD, ROWS = kRows;
   __shared__ __attribute__((aligned(1024))) char smem[2 * kSlots * kTile];
   char* const kring = smem;                   // K tile t in slot t % 4
   char* const vring = smem + kSlots * kTile;  // V tile t in slot t % 4
 
   const Work wk = VARLEN ? map_work_packed(blockIdx.x, B, Hq, Hkv, n_qt) : map_work(blockIdx.x, B, Hq, Hkv, n_qt);
-  const Slabs sl = slabs_of<VARLEN, D>(wk, q, k, v, o, lse, Hq, Hkv, Nq_all, Nk_all, vlen);
+  const Slabs sl = slabs_of<VARLEN>(wk, q, k, v, o, lse, Hq, Nq_all, Nk_all, vlen, ly);
   const int Nq = sl.Nq, Nk = sl.Nk;
   const int q0 = wk.qt * kBM;
   if (VARLEN && q0 >= Nq) return;  // past this sequence's rows (the whole workgroup)
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_d128_kernel(
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     if (qrow < Nq)
-      qop[ks] = *reinterpret_cast<const u32x4*>(qp + (size_t)qrow * D + 16 * ks + 8 * half);
+      qop[ks] = *reinterpret_cast<const u32x4*>(qp + (size_t)qrow * sl.qs + 16 * ks + 8 * half);
     else
       qop[ks] = u32x4{0u, 0u, 0u, 0u};
   }
@@ -237,19 +238,22 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_d128_kernel(
   const uint32_t lds_k = (uint32_t)(uintptr_t)(lds_void_t*)kring;
   const uint32_t lds_v = (uint32_t)(uintptr_t)(lds_void_t*)vring;
   const int wg = wv & 3;  // wave index within its group
-  const uint32_t dk = dma_src<false>(0, wg, lane, ROWS);  // source offsets of a full tile
-  const uint32_t dv = dma_src<true>(0, wg, lane, ROWS);
+  const uint32_t ksb = 2u * (uint32_t)sl.ks, vsb = 2u * (uint32_t)sl.vs;  // row strides in bytes
+  const uint32_t dk = dma_src<false>(0, wg, lane, ROWS, ksb);  // source offsets of a full tile
+  const uint32_t dv = dma_src<true>(0, wg, lane, ROWS, vsb);
+  const long long kstep = 16LL * sl.ks, vstep = 16LL * sl.vs;
   auto issue = [&](bool is_v, int t) {
     const int nvalid = min(ROWS, Nk - t * ROWS);
-    const uint16_t* base = (is_v ? vp : kp) + (size_t)t * ROWS * D;
+    const uint16_t* base = is_v ? vp + (long long)t * ROWS * sl.vs : kp + (long long)t * ROWS * sl.ks;
     const uint32_t slot = (is_v ? lds_v : lds_k) + (uint32_t)((t % kSlots) * kTile) + (uint32_t)(64 * wg * 16);
     if (nvalid == ROWS) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(base + 2048 * i, is_v ? dv : dk, slot + 4096 * i);
+      for (int i = 0; i < 4; ++i) dma16(base + (is_v ? vstep : kstep) * i, is_v ? dv : dk, slot + 4096 * i);
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        dma16(base, is_v ? dma_src<true>(i, wg, lane, nvalid) : dma_src<false>(i, wg, lane, nvalid), slot + 4096 * i);
+        dma16(base, is_v ? dma_src<true>(i, wg, lane, nvalid, vsb) : dma_src<false>(i, wg, lane, nvalid, ksb),
+              slot + 4096 * i);
     }
   };
   // Loads issued at the start of step i: K_{i+2} and V_{i+1}; returns the
@@ -291,10 +295,10 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_d128_kernel(
         // full phase: with full tiles the loads are spread over its MFMAs
         const bool spread = (!has_k || Nk - (i + 2) * ROWS >= ROWS) && (!has_v || Nk - (i + 1) * ROWS >= ROWS);
         if (!spread) issue_step(i);
-        const DmaSpread ex{kp + (size_t)(i + 2) * ROWS * D, vp + (size_t)(i + 1) * ROWS * D,
+        const DmaSpread ex{kp + (long long)(i + 2) * ROWS * sl.ks, vp + (long long)(i + 1) * ROWS * sl.vs,
                            lds_k + (uint32_t)(((i + 2) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
                            lds_v + (uint32_t)(((i + 1) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
-                           has_k && spread, has_v && spread, dk, dv};
+                           has_k && spread, has_v && spread, dk, dv, kstep, vstep};
         mma_run<DT, D, ROWS, true, true, DmaReader>(obuf, vring + ((i - 1) % kSlots) * kTile,
                                                     kring + (i % kSlots) * kTile, pk, qop, acc_o, s, lane, ex);
       } else {
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_d128_kernel(
   const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < Nq) {
-    uint16_t* orow = sl.o + (size_t)qrow * D;
+    uint16_t* orow = sl.o + (size_t)qrow * sl.os;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -350,7 +354,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   const Varlen vl{a.cu_q, a.cu_k, a.total_q, a.total_k};
   hipLaunchKernelGGL((fa_fwd_d128_kernel<DT, CAUSAL, VARLEN>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_qt, vl);
+                     a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_qt, vl, a.layout);
   return hipGetLastError();
 }
 

@@ -8,6 +8,12 @@
 
 namespace fa {
 
+// Element strides of (batch, head, row) for q, k, v and o; the head-dim
+// stride is 1. A packed batch uses the head and row (token) strides only.
+struct Layout {
+  long long q[3], k[3], v[3], o[3];
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -18,12 +24,14 @@ struct FwdArgs {
   float scale;
   int causal;
   int dtype;
-  // Packed variable-length batch (cu_q != nullptr): q, o [Hq, total_q, d],
-  // k, v [Hkv, total_k, d], lse [Hq, total_q]; Nq / Nk unused; query tiles
-  // cover max_seqlen_q rows per sequence.
+  // Packed variable-length batch (cu_q != nullptr): q, o hold total_q tokens
+  // per head, k, v total_k per kv-head (addressed through `layout`), lse
+  // [Hq, total_q]; Nq / Nk unused; query tiles cover max_seqlen_q rows per
+  // sequence.
   const int32_t* cu_q;
   const int32_t* cu_k;
   int total_q, total_k, max_seqlen_q;
+  Layout layout;
 };
 
 // Decode key split: chunk keys per workgroup, n_split chunks cover Lcap rows.

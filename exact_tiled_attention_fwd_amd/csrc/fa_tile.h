@@ -22,6 +22,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include "fa_launch.h"  // Layout
 
 namespace fa {
 
@@ -93,12 +94,12 @@ __device__ inline void unit_coords(int tid, int p, int& kq, int& c) {
   c = 4 * (wu % CG) + (lane >> 4);
 }
 
-// Loads of one tile by a group of 256 threads (tid in [0, 256)). Rows
-// [0, nvalid) of the tile are valid, nvalid >= 1; rows at or beyond nvalid
+// Loads of one tile by a group of 256 threads (tid in [0, 256)); rows are rs
+// elements apart. Rows [0, nvalid) of the tile are valid, nvalid >= 1; rows at or beyond nvalid
 // re-read row nvalid-1: their scores are masked to -inf, so they contribute
 // exactly 0, and no row past the valid range is ever touched.
 template <int D, int ROWS>
-__device__ inline void load_k(const uint16_t* __restrict__ kbase, int nvalid, int tid,
+__device__ inline void load_k(const uint16_t* __restrict__ kbase, int rs, int nvalid, int tid,
                               u32x4 (&rk)[TileRegs<D, ROWS>::KU]) {
   const bool full = nvalid >= ROWS;
 #pragma unroll
@@ -106,12 +107,12 @@ __device__ inline void load_k(const uint16_t* __restrict__ kbase, int nvalid, in
     int row, c;
     k_coords<D, ROWS>(tid, p, row, c);
     if (!full) row = min(row, nvalid - 1);
-    rk[p] = *reinterpret_cast<const u32x4*>(kbase + (size_t)row * D + (size_t)c * 8);
+    rk[p] = *reinterpret_cast<const u32x4*>(kbase + (size_t)row * rs + (size_t)c * 8);
   }
 }
 
 template <int D, int ROWS>
-__device__ inline void load_v(const uint16_t* __restrict__ vbase, int nvalid, int tid,
+__device__ inline void load_v(const uint16_t* __restrict__ vbase, int rs, int nvalid, int tid,
                               u32x4 (&rv)[Tile<D, ROWS>::U][4]) {
   const bool full = nvalid >= ROWS;
 #pragma unroll
@@ -122,16 +123,9 @@ __device__ inline void load_v(const uint16_t* __restrict__ vbase, int nvalid, in
     for (int i = 0; i < 4; ++i) {
       int row = 4 * kq + i;
       if (!full) row = min(row, nvalid - 1);
-      rv[p][i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)row * D + (size_t)c * 8);
+      rv[p][i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)row * rs + (size_t)c * 8);
     }
   }
-}
-
-template <int D, int ROWS>
-__device__ inline void load_tile(const uint16_t* __restrict__ kbase, const uint16_t* __restrict__ vbase,
-                                 int nvalid, TileRegs<D, ROWS>& r) {
-  load_k<D, ROWS>(kbase, nvalid, threadIdx.x, r.k);
-  load_v<D, ROWS>(vbase, nvalid, threadIdx.x, r.v);
 }
 
 // Position (in elements) of key kk (0..15) inside its 16-key group of V^T: the
@@ -494,7 +488,8 @@ struct Varlen {
   int total_q, total_k;
 };
 
-// The slabs one workgroup reads and writes, with their row counts.
+// The slabs one workgroup reads and writes, with their row counts and row
+// strides (elements).
 struct Slabs {
   const uint16_t* q;
   const uint16_t* k;
@@ -502,38 +497,43 @@ struct Slabs {
   uint16_t* o;
   float* lse;  // null: not written
   int Nq, Nk;
+  int qs, ks, vs, os;
 };
 
-// Fixed layout: q, o [B, Hq, Nq, D]; k, v [B, Hkv, Nk, D]; lse [B, Hq, Nq].
-// Packed layout: offsets are clamped into [0, total] and made non-decreasing,
+// Fixed layout: row i of (b, h) of q at q + b ly.q[0] + h ly.q[1] + i ly.q[2]
+// (likewise k, v with the kv-head, and o); lse [B, Hq, Nq].
+// Packed layout: token t of head h at q + h ly.q[1] + t ly.q[2]; lse
+// [Hq, total_q]. Offsets are clamped into [0, total] and made non-decreasing,
 // so no offset array, however wrong, leads outside the tensors.
-template <bool VARLEN, int D>
+template <bool VARLEN>
 __device__ inline Slabs slabs_of(const Work& w, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
-                                 float* lse, int Hq, int Hkv, int Nq, int Nk, const Varlen& vl) {
+                                 float* lse, int Hq, int Nq, int Nk, const Varlen& vl, const Layout& ly) {
   Slabs s;
   if constexpr (VARLEN) {
     const int q_lo = min(max(vl.cu_q[w.b], 0), vl.total_q);
     const int q_hi = min(max(vl.cu_q[w.b + 1], q_lo), vl.total_q);
     const int k_lo = min(max(vl.cu_k[w.b], 0), vl.total_k);
     const int k_hi = min(max(vl.cu_k[w.b + 1], k_lo), vl.total_k);
-    const size_t qoff = ((size_t)w.h * vl.total_q + q_lo), koff = ((size_t)w.g * vl.total_k + k_lo);
-    s.q = q + qoff * D;
-    s.o = o + qoff * D;
-    s.lse = lse ? lse + qoff : nullptr;
-    s.k = k + koff * D;
-    s.v = v + koff * D;
+    s.q = q + w.h * ly.q[1] + q_lo * ly.q[2];
+    s.o = o + w.h * ly.o[1] + q_lo * ly.o[2];
+    s.lse = lse ? lse + (size_t)w.h * vl.total_q + q_lo : nullptr;
+    s.k = k + w.g * ly.k[1] + k_lo * ly.k[2];
+    s.v = v + w.g * ly.v[1] + k_lo * ly.v[2];
     s.Nq = q_hi - q_lo;
     s.Nk = k_hi - k_lo;
   } else {
-    const size_t bh = (size_t)w.b * Hq + w.h, bg = (size_t)w.b * Hkv + w.g;
-    s.q = q + bh * Nq * D;
-    s.o = o + bh * Nq * D;
-    s.lse = lse ? lse + bh * Nq : nullptr;
-    s.k = k + bg * Nk * D;
-    s.v = v + bg * Nk * D;
+    s.q = q + w.b * ly.q[0] + w.h * ly.q[1];
+    s.o = o + w.b * ly.o[0] + w.h * ly.o[1];
+    s.lse = lse ? lse + ((size_t)w.b * Hq + w.h) * Nq : nullptr;
+    s.k = k + w.b * ly.k[0] + w.g * ly.k[1];
+    s.v = v + w.b * ly.v[0] + w.g * ly.v[1];
     s.Nq = Nq;
     s.Nk = Nk;
   }
+  s.qs = (int)ly.q[2];
+  s.ks = (int)ly.k[2];
+  s.vs = (int)ly.v[2];
+  s.os = (int)ly.o[2];
   return s;
 }
 

@@ -114,6 +114,58 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
                         int d, float scale, int causal, int dtype, void* stream);
 
 /*
+ * fa_fwd_strided - fa_fwd with q, k, v and o at any element strides, e.g. the
+ * (batch, seq, heads, dim) layout.
+ *
+ * Source: "FlashAttention complete guide for beginners" (cloud-allstudy
+ * tistory), section 5 "Usage (code examples)": flash_attn_func takes q, k, v
+ * laid out (batch, seq, heads, dim); the SDPA page (devhandbook.co.kr),
+ * Example 1, lays the same tensors out (B, H, L, D). The operation is the
+ * one of fa_fwd; only the addressing differs, and the result is bitwise that
+ * of fa_fwd on the same values.
+ *
+ *   strides  host array of 12 int64: the element strides of (batch, head,
+ *            row) for q, then k, v and o. Element (b, h, i, c) of q is at
+ *            q + b*strides[0] + h*strides[1] + i*strides[2] + c. Every stride
+ *            is a non-negative multiple of 8 (16-byte rows); row strides are
+ *            below 2^24 and the others below 2^40. The strides of o must not
+ *            make two of its elements share memory; o must not overlap q, k
+ *            or v (checked on the spans the strides reach).
+ *            The (batch, seq, heads, dim) layout is {Nq*Hq*d, d, Hq*d} for q
+ *            and o and {Nk*Hkv*d, d, Hkv*d} for k and v.
+ *   lse      [B, Hq, Nq] fp32, contiguous, or NULL.
+ *   all other arguments as in fa_fwd.
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+fa_status fa_fwd_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const int64_t* strides, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                         float scale, int causal, int dtype, void* stream);
+
+/*
+ * fa_fwd_varlen_strided - fa_fwd_varlen with q, k, v and o at any element
+ * strides, e.g. the packed (total, heads, dim) layout.
+ *
+ * Source: as fa_fwd_varlen ("Continuous batching", cabseo.com) with the
+ * addressing of fa_fwd_strided.
+ *
+ *   strides  host array of 8 int64: the element strides of (head, token) for
+ *            q, then k, v and o; token t of head h of q is at
+ *            q + h*strides[0] + t*strides[1]. The (total, heads, dim) layout
+ *            is {d, Hq*d} for q and o and {d, Hkv*d} for k and v. Same rules
+ *            as in fa_fwd_strided.
+ *   lse      [Hq, total_q] fp32, contiguous, or NULL.
+ *   all other arguments as in fa_fwd_varlen.
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+fa_status fa_fwd_varlen_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int64_t* strides, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_k, int B, int Hq, int Hkv, int total_q,
+                                int total_k, int max_seqlen_q, int d, float scale, int causal,
+                                int dtype, void* stream);
+
+/*
  * fa_decode_workspace_bytes - bytes of device workspace fa_decode needs for
  * these sizes and this `num_splits` (0 = the library's choice). Returns 0 if
  * the sizes are invalid. The workspace holds per-split partial outputs and

@@ -29,8 +29,8 @@ def test_library_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"fa_fwd", "fa_fwd_varlen", "fa_decode", "fa_decode_paged", "fa_decode_workspace_bytes",
-            "fa_status_string", "fa_last_error"} <= set(names)
+    assert {"fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_varlen_strided", "fa_decode", "fa_decode_paged",
+            "fa_decode_workspace_bytes", "fa_status_string", "fa_last_error"} <= set(names)
     raw = ctypes.CDLL(fa.lib_path())
     for n in names:
         assert hasattr(raw, n), f"{n} declared in fa.h but not exported"
@@ -136,6 +136,81 @@ def test_fwd_varlen_rejects_before_launch(kw, status):
     assert st == status, (st, fa.fa_last_error())
 
 
+# (batch, seq, heads, dim) strides of q/o [B=2, N=256, Hq=8, d=64] and k/v [B=2, N=256, Hkv=2, d=64]
+BSHD = [256 * 8 * 64, 64, 8 * 64, 256 * 2 * 64, 64, 2 * 64, 256 * 2 * 64, 64, 2 * 64, 256 * 8 * 64, 64, 8 * 64]
+
+
+def fwd_strided(strides=BSHD, **kw):
+    a = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, o=FAKE + 0x3000000, lse=None,
+             B=2, Hq=8, Hkv=2, Nq=256, Nk=256, d=64, scale=0.125, causal=1, dtype=0, stream=None)
+    a.update(kw)
+    if strides is None:
+        lib = fa.load_library()
+        return lib.fa_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], None, a["B"], a["Hq"], a["Hkv"],
+                                  a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+    return fa.fa_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], strides, a["B"], a["Hq"], a["Hkv"],
+                             a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+def _with(i, x):
+    s = list(BSHD)
+    s[i] = x
+    return s
+
+
+@pytest.mark.parametrize("strides,kw,status", [
+    (None, {}, fa.FA_ERR_INVALID_ARG),                        # no stride array
+    (_with(2, -512), {}, fa.FA_ERR_INVALID_ARG),              # negative row stride of q
+    (_with(4, 60), {}, fa.FA_ERR_INVALID_ARG),                # k head stride not a multiple of 8
+    (_with(8, 1 << 24), {}, fa.FA_ERR_INVALID_ARG),           # v row stride too large
+    (_with(11, 32), {}, fa.FA_ERR_INVALID_ARG),               # o rows overlap each other (32 < d)
+    (_with(10, 0), {}, fa.FA_ERR_INVALID_ARG),                # every o head writes the same rows
+    (_with(9, 1 << 40), {}, fa.FA_ERR_INVALID_ARG),           # o batch stride too large
+    (BSHD, dict(o=FAKE + 0x400), fa.FA_ERR_INVALID_ARG),      # o inside the span of q
+    (BSHD, dict(lse=FAKE + 0x2000100), fa.FA_ERR_INVALID_ARG),  # lse inside the span of v
+    (BSHD, dict(causal=1, Nq=257), fa.FA_ERR_INVALID_ARG),    # causal needs Nq <= Nk
+    (BSHD, dict(d=96), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fwd_strided_rejects_before_launch(strides, kw, status):
+    st = fwd_strided(strides, **kw)
+    assert st == status, (st, fa.fa_last_error())
+    assert fa.fa_last_error() != ""
+
+
+def fwd_varlen_strided(strides, **kw):
+    a = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, o=FAKE + 0x3000000, lse=None,
+             cu_q=FAKE + 0x4000000, cu_k=FAKE + 0x4100000, B=3, Hq=8, Hkv=2, total_q=1000, total_k=1200,
+             max_q=600, d=128, scale=0.088, causal=1, dtype=0, stream=None)
+    a.update(kw)
+    return fa.fa_fwd_varlen_strided(a["q"], a["k"], a["v"], a["o"], a["lse"], strides, a["cu_q"], a["cu_k"], a["B"],
+                                    a["Hq"], a["Hkv"], a["total_q"], a["total_k"], a["max_q"], a["d"], a["scale"],
+                                    a["causal"], a["dtype"], a["stream"])
+
+
+THD = [128, 8 * 128, 128, 2 * 128, 128, 2 * 128, 128, 8 * 128]  # (total, heads, dim)
+
+
+@pytest.mark.parametrize("strides,kw,status", [
+    ([THD[0], -THD[1]] + THD[2:], {}, fa.FA_ERR_INVALID_ARG),
+    (THD[:7] + [64], {}, fa.FA_ERR_INVALID_ARG),              # o tokens overlap
+    (THD[:6] + [0, THD[7]], {}, fa.FA_ERR_INVALID_ARG),       # o heads alias
+    (THD, dict(cu_q=None), fa.FA_ERR_INVALID_ARG),
+    (THD, dict(o=FAKE + 0x800), fa.FA_ERR_INVALID_ARG),       # o inside q
+    (THD, dict(max_q=1001), fa.FA_ERR_INVALID_ARG),
+])
+def test_fwd_varlen_strided_rejects_before_launch(strides, kw, status):
+    st = fwd_varlen_strided(strides, **kw)
+    assert st == status, (st, fa.fa_last_error())
+
+
+def test_fwd_strided_needs_its_stride_count():
+    with pytest.raises(ValueError):
+        fa.fa_fwd_strided(FAKE, FAKE, FAKE, FAKE, None, [64] * 11, 1, 1, 1, 8, 8, 64, 0.1, 0, 0, None)
+    with pytest.raises(ValueError):
+        fa.fa_fwd_varlen_strided(FAKE, FAKE, FAKE, FAKE, None, [64] * 7, FAKE, FAKE, 1, 1, 1, 8, 8, 8, 64, 0.1, 0,
+                                 0, None)
+
+
 def dec_paged(**kw):
     a = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, table=FAKE + 0x2800000, seqlens=FAKE + 0x3000000,
              o=FAKE + 0x3100000, lse=None, ws=FAKE + 0x4000000, ws_bytes=1 << 30, B=2, Hq=8, Hkv=2,
@@ -182,3 +257,8 @@ def test_python_helpers_validate_tensors():
         fa.attention(torch.zeros(1, 1, 4, 64), torch.zeros(1, 1, 4, 64), torch.zeros(1, 1, 4, 64))
     with pytest.raises(NotImplementedError):
         fa.dtype_code(torch.float32)
+    with pytest.raises(NotImplementedError):   # dropout is not part of the forward path
+        fa.flash_attn_func(torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64),
+                           dropout_p=0.1)
+    with pytest.raises(ValueError):            # host tensors are refused
+        fa.flash_attn_func(torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64))
