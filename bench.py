@@ -48,8 +48,12 @@ import attn_inputs as ai  # noqa: E402
 MFMA_PEAK_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = [os.path.join(ROOT, "exact_tiled_attention_fwd_amd", "csrc", f)
+CSRC = os.path.join(ROOT, "exact_tiled_attention_fwd_amd", "csrc")
+KERNEL_SOURCES = [os.path.join(CSRC, f)
                   for f in ("fa_tile.h", "fa_fwd.hip", "fa_fwd_d128.hip", "fa_decode.hip", "fa_launch.h", "fa_api.cpp")]
+# The device code behind each measured kernel (its counter summary records these).
+FWD_D128_SOURCES = ("fa_fwd_d128.hip", "fa_tile.h", "fa_launch.h")
+DECODE_SOURCES = ("fa_decode.hip", "fa_tile.h", "fa_launch.h")
 
 
 def log(*a):
@@ -79,24 +83,29 @@ def kv_cache_bytes(seq_len, layers, hidden, bytes_per_value):
     return seq_len * 2 * layers * hidden * bytes_per_value
 
 
-def kernel_source_hash():
+def kernel_source_hash(files=None):
+    """sha256 prefix over the named csrc files (default: all kernel sources)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    paths = KERNEL_SOURCES if files is None else [os.path.join(CSRC, f) for f in files]
+    for p in paths:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
 def counter_traffic(name):
-    """HBM bytes per launch from a committed counter summary, if it matches
-    the current kernel sources; else None."""
+    """HBM bytes per launch from a committed counter summary, if the kernel
+    sources it names still hash to the recorded value; else None."""
     path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
     text = open(path).read()
+    m_files = re.search(r"kernel_sources:\s*(.+)", text)
     m_src = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_src or not m_b or m_src.group(1) != kernel_source_hash():
+    if not m_files or not m_src or not m_b:
+        return None
+    if m_src.group(1) != kernel_source_hash(m_files.group(1).split()):
         return None
     return float(m_b.group(1))
 
