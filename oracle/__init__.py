@@ -1,4 +1,4 @@
-"""CPU oracle for exact attention forward and KV-cache decode (TEST INFRASTRUCTURE).
+"""CPU oracle for exact attention forward, its gradients and KV-cache decode (TEST INFRASTRUCTURE).
 
 Plain, slow, float64 NumPy code that materialises the full score matrix. It is
 the yardstick the HIP kernels are checked against and is never part of the
@@ -7,7 +7,8 @@ leg of ``bench.py`` may import it. It shares no code with the GPU library;
 both sides draw their inputs from ``attn_inputs`` only.
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
-closed forms, invariants, a pure-Python brute force and hand-worked fixtures.
+closed forms, invariants, a pure-Python brute force and hand-worked fixtures;
+the gradients against central finite differences of the forward.
 No page prints numeric attention outputs, so beyond those pins the large
 random configurations are pinned only through this oracle.
 """
@@ -16,3 +17,4 @@ from .exact import (  # noqa: F401
     attention_rows, attention_varlen, decode, decode_paged,
 )
 from .blockwise import blockwise_attention_head, merge_partials  # noqa: F401
+from .backward import attention_head_bwd, attention_bwd  # noqa: F401

@@ -400,10 +400,108 @@ def pin_varlen_is_per_sequence():
     assert np.array_equal(Oc, Od) and np.array_equal(Lc, Ld) and np.all(np.isfinite(Lc))
 
 
+# ---------------------------------------------------------------- backward
+def _loss_grad_fd(q, k, v, do, scale, causal, eps=1e-6):
+    """Central finite differences of L = sum(dO * O) through the forward oracle,
+    for each element of q, k and v in turn."""
+    def loss(args):
+        O, _ = oracle.attention(*args, scale, causal)
+        return float(np.sum(do * O))
+    grads = []
+    for which in range(3):
+        base = [q, k, v]
+        t = base[which]
+        g = np.zeros_like(t)
+        for idx in np.ndindex(t.shape):
+            tp, tm = t.copy(), t.copy()
+            tp[idx] += eps
+            tm[idx] -= eps
+            g[idx] = (loss([tp if i == which else base[i] for i in range(3)])
+                      - loss([tm if i == which else base[i] for i in range(3)])) / (2 * eps)
+        grads.append(g)
+    return grads
+
+
+def pin_bwd_finite_differences():
+    """The backward oracle is the derivative of the forward oracle: central
+    differences of sum(dO * O) on tiny GQA inputs, causal (with Nq < Nk) and
+    not."""
+    r = _rng(61)
+    for causal, (Nq, Nk) in ((False, (5, 7)), (True, (5, 7)), (True, (6, 6))):
+        q = r.standard_normal((1, 2, Nq, 4))
+        k = r.standard_normal((1, 1, Nk, 4))
+        v = r.standard_normal((1, 1, Nk, 4))
+        do = r.standard_normal((1, 2, Nq, 4))
+        dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.7, causal)
+        fq, fk, fv = _loss_grad_fd(q, k, v, do, 0.7, causal)
+        for a, b in ((dq, fq), (dk, fk), (dv, fv)):
+            assert a.shape == b.shape
+            assert np.max(np.abs(a - b)) < 1e-7 * max(1.0, np.max(np.abs(b))), np.max(np.abs(a - b))
+
+
+def pin_bwd_equal_value_rows():
+    """If every V row is the same vector, O does not depend on the scores, so
+    dQ = dK = 0 exactly (up to rounding), and dV_j = sum_i P_ij dO_i."""
+    r = _rng(62)
+    q = r.standard_normal((1, 2, 9, 8))
+    k = r.standard_normal((1, 2, 11, 8))
+    v = np.broadcast_to(r.standard_normal(8), (1, 2, 11, 8)).copy()
+    do = r.standard_normal((1, 2, 9, 8))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.4, True)
+    assert np.max(np.abs(dq)) < 1e-12 and np.max(np.abs(dk)) < 1e-12
+    # dV sums over queries: column sums equal those of dO
+    assert np.allclose(dv.sum(axis=2), do.sum(axis=2), atol=1e-12)
+
+
+def pin_bwd_dv_column_sums_and_causal_row0():
+    """Rows of P sum to one, so the key-sum of dV equals the query-sum of dO;
+    a causal first row (Nq = Nk) sees only key 0, so its dQ is zero; the last
+    key is seen only by the last row, so its dV is that row's dO weighted by
+    the row's softmax weight on it (a direct softmax of one score row)."""
+    r = _rng(63)
+    B, Hq, Hkv, N, d, sc = 2, 4, 2, 12, 8, 0.3
+    q = r.standard_normal((B, Hq, N, d))
+    k = r.standard_normal((B, Hkv, N, d))
+    v = r.standard_normal((B, Hkv, N, d))
+    do = r.standard_normal((B, Hq, N, d))
+    grp = Hq // Hkv
+    for causal in (False, True):
+        dq, dk, dv = oracle.attention_bwd(q, k, v, do, sc, causal)
+        assert np.allclose(dv.sum(axis=2), do.reshape(B, Hkv, grp, N, d).sum(axis=(2, 3)), atol=1e-12)
+    assert np.max(np.abs(dq[:, :, 0])) < 1e-14
+    sigma = float(np.float32(sc))
+    for b in range(B):
+        for g in range(Hkv):
+            want = np.zeros(d)
+            for h in range(g * grp, (g + 1) * grp):
+                row = [sigma * sum(q[b, h, -1, t] * k[b, g, j, t] for t in range(d)) for j in range(N)]
+                mx = max(row)
+                w = [math.exp(x - mx) for x in row]
+                want += (w[-1] / sum(w)) * do[b, h, -1]
+            assert np.allclose(dv[b, g, -1], want, atol=1e-12)
+
+
+def pin_bwd_gqa_is_repeated_mha():
+    """Grouped heads: a kv-head's dK and dV are the sums over its q-heads of
+    the gradients with K and V repeated per q-head."""
+    r = _rng(64)
+    q = r.standard_normal((1, 6, 7, 8))
+    k = r.standard_normal((1, 2, 9, 8))
+    v = r.standard_normal((1, 2, 9, 8))
+    do = r.standard_normal((1, 6, 7, 8))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.5, True)
+    kr, vr = np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1)
+    dq2, dk2, dv2 = oracle.attention_bwd(q, kr, vr, do, 0.5, True)
+    assert np.allclose(dq, dq2, atol=1e-13)
+    assert np.allclose(dk, dk2.reshape(1, 2, 3, 9, 8).sum(axis=2), atol=1e-13)
+    assert np.allclose(dv, dv2.reshape(1, 2, 3, 9, 8).sum(axis=2), atol=1e-13)
+
+
 ALL_PINS = [
     pin_brute_force, pin_single_key_and_causal_row0, pin_two_keys, pin_golden_fixtures,
     pin_zero_query, pin_rows_sum_to_one, pin_merge_identity, pin_shift_invariance,
     pin_permutation, pin_convex_hull, pin_causal_is_prefix, pin_gqa_is_repeated_mha,
     pin_decode_is_single_query, pin_lse_library, pin_sampled_rows_match_full,
-    pin_paged_decode_is_decode, pin_varlen_is_per_sequence,
+    pin_paged_decode_is_decode, pin_varlen_is_per_sequence, pin_bwd_finite_differences,
+    pin_bwd_equal_value_rows, pin_bwd_dv_column_sums_and_causal_row0, pin_bwd_gqa_is_repeated_mha,
 ]

@@ -149,7 +149,53 @@ def _scale_not_rounded(scale):
     return float(scale)
 
 
+from oracle import backward as obw  # noqa: E402
+
+
+def _bwd_variant(mistake):
+    """attention_head_bwd with one planted mistake."""
+    def f(q, k, v, do, scale, causal=False):
+        q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
+        s = oe.as_fp32_scale(scale)
+        P, _, _ = oe.softmax_rows(oe.scores(q, k, scale), oe.visibility(q.shape[0], k.shape[0], causal))
+        O = P @ v
+        dV = P.T @ do
+        dP = do @ v.T
+        D = np.sum(do * O, axis=1)
+        if mistake == "no_D":
+            dS = P * dP
+        elif mistake == "D_sign":
+            dS = P * (dP + D[:, None])
+        else:
+            dS = P * (dP - D[:, None])
+        dQ = (dS @ k) if mistake == "dq_no_scale" else s * (dS @ k)
+        dK = s * (dS.T @ q)
+        if mistake == "dk_from_dp":
+            dK = s * ((P * dP).T @ q)
+        if mistake == "dv_from_o":
+            dV = P.T @ (do - O)
+        return dQ, dK, dV
+    return f
+
+
+def _bwd_gqa_overwrite(q, k, v, do, scale, causal=False):
+    B, Hq = q.shape[:2]
+    Hkv = k.shape[1]
+    dQ, dK, dV = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            dQ[b, h], dK[b, g], dV[b, g] = obw.attention_head_bwd(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal)
+    return dQ, dK, dV
+
+
 MUTATIONS = [
+    ("bwd_no_D", obw, "attention_head_bwd", _bwd_variant("no_D")),
+    ("bwd_D_sign", obw, "attention_head_bwd", _bwd_variant("D_sign")),
+    ("bwd_dq_no_scale", obw, "attention_head_bwd", _bwd_variant("dq_no_scale")),
+    ("bwd_dk_from_dp", obw, "attention_head_bwd", _bwd_variant("dk_from_dp")),
+    ("bwd_dv_from_o", obw, "attention_head_bwd", _bwd_variant("dv_from_o")),
+    ("bwd_gqa_overwrite", oracle, "attention_bwd", _bwd_gqa_overwrite),
     ("scores_no_scale", oe, "scores", _scores_no_scale),
     ("scores_transposed", oe, "scores", _scores_transposed),
     ("scores_wrong_sign", oe, "scores", _scores_wrong_sign),
