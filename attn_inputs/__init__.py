@@ -12,7 +12,8 @@ cabseo.com, section "Memory requirements") gives the per-sequence cache that
 decode reads.
 
 Seeding: every (tensor, batch, head) slab has its own NumPy substream
-``default_rng([seed, tensor_id, b, head])`` with tensor_id Q=0, K=1, V=2, so a
+``default_rng([seed, tensor_id, b, head])`` with tensor_id Q=0, K=1, V=2 and
+the upstream gradient dO=9 (backward workloads), so a
 slab can be regenerated alone (long-context row samples, per-head oracles).
 Values are float32 ``standard_normal`` draws in row-major (row, dim) order,
 rounded to nearest-even into bf16 or fp16.
@@ -25,7 +26,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 __all__ = [
-    "BF16", "FP16", "Q_ID", "K_ID", "V_ID",
+    "BF16", "FP16", "Q_ID", "K_ID", "V_ID", "DO_ID", "grad_output",
     "round_to_bits", "bits_to_f64", "slab", "prefill_inputs",
     "decode_lengths", "decode_inputs", "paged_layout", "varlen_inputs", "sample_rows", "CONFIGS",
 ]
@@ -33,6 +34,7 @@ __all__ = [
 BF16 = "bf16"
 FP16 = "fp16"
 Q_ID, K_ID, V_ID = 0, 1, 2
+DO_ID = 9  # upstream gradient of O
 BF16_NAN_BITS = 0x7FC0
 FP16_NAN_BITS = 0x7E00
 
@@ -115,6 +117,14 @@ def prefill_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, dtype: 
     _fill(k, seed, K_ID, Nk, d, dtype)
     _fill(v, seed, V_ID, Nk, d, dtype)
     return dict(q=q, k=k, v=v, dtype=dtype)
+
+
+def grad_output(seed: int, B: int, Hq: int, N: int, d: int, dtype: str) -> np.ndarray:
+    """dO [B,Hq,N,d] as uint16 bits: the upstream gradient of O for backward
+    workloads, N(0,1) like the inputs."""
+    do = np.empty((B, Hq, N, d), np.uint16)
+    _fill(do, seed, DO_ID, N, d, dtype)
+    return do
 
 
 def decode_lengths(seed: int, B: int, lo: int, hi: int) -> np.ndarray:

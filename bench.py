@@ -145,6 +145,34 @@ class Prefill:
         self.fa.attention(self.q, self.k, self.v, causal=self.causal, out=self.o, lse=self.lse)
 
 
+class Backward:
+    """dQ, dK, dV of one prefill layer (fa_bwd: delta, dK/dV and dQ kernels),
+    with O and LSE from the forward and a seeded N(0,1) upstream gradient.
+    FLOPs count the five products of the gradient (2.5x the forward's)."""
+
+    def __init__(self, fa, name, causal):
+        import torch
+        c = ai.CONFIGS[name]
+        self.fa, self.causal = fa, causal
+        B, Hq, Hkv, N, d, dt = c["B"], c["Hq"], c["Hkv"], c["N"], c["d"], c["dtype"]
+        t0 = time.time()
+        x = ai.prefill_inputs(c["seed"], B, Hq, Hkv, N, d, dt)
+        self.q, self.k, self.v = to_dev(x["q"], dt), to_dev(x["k"], dt), to_dev(x["v"], dt)
+        del x
+        self.do = to_dev(ai.grad_output(c["seed"], B, Hq, N, d, dt), dt)
+        self.o, self.lse = fa.attention(self.q, self.k, self.v, causal=causal)
+        self.dq, self.dk, self.dv = (torch.empty_like(t) for t in (self.q, self.k, self.v))
+        self.ws = torch.empty(fa.fa_bwd_workspace_bytes(B, Hq, N), dtype=torch.uint8, device="cuda")
+        self.flops = 2.5 * prefill_flops(B, Hq, N, N, d, causal)
+        # reads q, k, v, o, dO, lse; writes dq, dk, dv
+        self.bytes = 2 * (4 * B * Hq * N * d + 4 * B * Hkv * N * d) + 4 * B * Hq * N
+        log(f"[bench] {name} backward causal={causal}: inputs ready in {time.time() - t0:.1f}s")
+
+    def __call__(self):
+        self.fa.attention_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, causal=self.causal,
+                              dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws)
+
+
 class PrefillVarlen:
     """Packed causal prefill: 16 Llama-3-shaped sequences of seeded lengths,
     one slab per head, no padding. FLOPs sum the per-sequence counts."""
@@ -293,6 +321,27 @@ def cpu_baseline_prefill(name="llama3_8b_gqa_n8192", heads=32):
                       f"(float64 NumPy, score matrix materialised); {elapsed:.1f}s"}
 
 
+def cpu_baseline_backward(name="llama3_8b_gqa_n8192", heads=4):
+    """The gradient oracle on `heads` q-heads (one kv-head group) of the
+    backward workload, all rows and keys, causal: TFLOP/s by the GPU's FLOP
+    convention (2.5x the forward's)."""
+    import oracle
+    c = ai.CONFIGS[name]
+    N, d, dt = c["N"], c["d"], c["dtype"]
+    f = lambda a: ai.bits_to_f64(a, dt)
+    q = np.stack([f(ai.slab(c["seed"], ai.Q_ID, 0, h, N, d, dt)) for h in range(heads)])[None]
+    do = np.stack([f(ai.slab(c["seed"], ai.DO_ID, 0, h, N, d, dt)) for h in range(heads)])[None]
+    k = f(ai.slab(c["seed"], ai.K_ID, 0, 0, N, d, dt))[None, None]
+    v = f(ai.slab(c["seed"], ai.V_ID, 0, 0, N, d, dt))[None, None]
+    t0 = time.perf_counter()
+    oracle.attention_bwd(q, k, v, do, 1.0 / math.sqrt(d), True)
+    elapsed = time.perf_counter() - t0
+    flops = 2.5 * prefill_flops(1, heads, N, N, d, True)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cpu_cores_used(), "kind": "oracle",
+            "sample": f"{heads} of 32 q-heads (kv-head 0's group) of the N=8192 causal layer, all rows and keys "
+                      f"(float64 NumPy gradients, score matrix materialised); {elapsed:.1f}s"}
+
+
 def cpu_baseline_varlen(name="llama3_8b_gqa_varlen", seqs=16, heads=4):
     """The oracle's packed prefill on the first `seqs` sequences, `heads`
     q-heads each (all rows, causal): TFLOP/s by the GPU's FLOP convention."""
@@ -401,19 +450,25 @@ def main():
 
     cfg = args.config
     run_prefill = cfg in ("default", "tiny_mha_n128", "mha_n4096_fp16", "mha_n4096_fp16_causal", "llama3_8b_gqa_n8192",
-                          "llama3_8b_gqa_n131072", "llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd")
+                          "llama3_8b_gqa_n131072", "llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd",
+                          "llama3_8b_gqa_n8192_bwd")
     run_decode = cfg in ("default", "decode_32seq_gqa", "decode_32seq_gqa_paged")
     paged = cfg == "decode_32seq_gqa_paged"
     if not (run_prefill or run_decode):
         raise SystemExit(f"unknown --config {cfg}")
-    pname = "llama3_8b_gqa_n8192" if cfg in ("default", "llama3_8b_gqa_n8192_bshd") else cfg.replace("_causal", "")
+    pname = ("llama3_8b_gqa_n8192" if cfg in ("default", "llama3_8b_gqa_n8192_bshd", "llama3_8b_gqa_n8192_bwd")
+             else cfg.replace("_causal", ""))
     causal = cfg in ("default", "llama3_8b_gqa_n8192", "llama3_8b_gqa_n131072", "mha_n4096_fp16_causal",
-                     "llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd")
+                     "llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd", "llama3_8b_gqa_n8192_bwd")
     parts = []
     pre = dec = None
     if run_prefill:
-        pre = (PrefillVarlen(fa) if cfg == "llama3_8b_gqa_varlen"
-               else Prefill(fa, pname, causal, layout="bshd" if cfg.endswith("_bshd") else "bhnd"))
+        if cfg == "llama3_8b_gqa_varlen":
+            pre = PrefillVarlen(fa)
+        elif cfg.endswith("_bwd"):
+            pre = Backward(fa, pname, causal)
+        else:
+            pre = Prefill(fa, pname, causal, layout="bshd" if cfg.endswith("_bshd") else "bhnd")
         parts.append(pre)
     if run_decode:
         dec = DecodePaged(fa, num_splits=args.num_splits) if paged else Decode(fa, num_splits=args.num_splits)
@@ -427,11 +482,11 @@ def main():
         t_ms = float(np.mean(per[i]))
         tflops = pre.flops / (t_ms * 1e-3) / 1e12
         out.update(value=round(tflops, 2), unit="TFLOP/s")
-        wl = cfg if cfg in ("llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd") else pname
+        wl = cfg if cfg in ("llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd", "llama3_8b_gqa_n8192_bwd") else pname
         out["prefill"] = {"workload": f"{wl} causal={causal}", "ms_mean": round(t_ms, 4),
                           "ms_min": round(float(np.min(per[i])), 4), "tflops": round(tflops, 2),
                           "frac_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS, 4)}
-        prof = cfg if cfg in ("llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd") else pname
+        prof = cfg if cfg in ("llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd", "llama3_8b_gqa_n8192_bwd") else pname
         traffic = counter_traffic(f"fa_fwd_{prof}_counters.md") if causal else None
         out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
@@ -458,6 +513,8 @@ def main():
     if not args.no_cpu_baseline:
         if cfg == "llama3_8b_gqa_varlen":
             out["cpu_baseline"] = cpu_baseline_varlen()
+        elif cfg == "llama3_8b_gqa_n8192_bwd":
+            out["cpu_baseline"] = cpu_baseline_backward()
         elif pre is not None and pname == "llama3_8b_gqa_n8192":
             out["cpu_baseline"] = cpu_baseline_prefill()
             if dec is not None:

@@ -6,9 +6,9 @@ runs in the HIP kernels of that library; this module only marshals arguments.
 PyTorch supplies device memory and the current stream.
 
 Raw entry points, same names and argument order as the C header:
-    fa_fwd, fa_fwd_strided, fa_fwd_varlen, fa_fwd_varlen_strided, fa_decode,
-    fa_decode_paged, fa_decode_workspace_bytes, fa_status_string,
-    fa_last_error, fa_abi_version
+    fa_fwd, fa_fwd_strided, fa_fwd_varlen, fa_fwd_varlen_strided, fa_bwd,
+    fa_bwd_workspace_bytes, fa_decode, fa_decode_paged,
+    fa_decode_workspace_bytes, fa_status_string, fa_last_error, fa_abi_version
 Tensor-level helpers:
     attention(q, k, v, causal=False, scale=None) -> (o, lse)
         q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d], any strides with a unit last one
@@ -20,6 +20,8 @@ Tensor-level helpers:
     flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                            max_seqlen_k, dropout_p=0.0, softmax_scale=None,
                            causal=False) -> o, for q [total_q,Hq,d]
+    attention_bwd(q, k, v, o, lse, dout, causal=False, scale=None)
+        -> (dq, dk, dv), for the contiguous layouts of attention()
     decode(q, k_cache, v_cache, seqlens, scale=None, num_splits=0) -> (o, lse)
     decode_paged(q, k_pages, v_pages, block_table, seqlens, scale=None,
                  num_splits=0) -> (o, lse)
@@ -38,7 +40,8 @@ import torch  # loads the HIP runtime that libfa.so then binds to
 __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
     "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FAError", "lib_path", "load_library",
-    "fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_varlen_strided", "fa_decode", "fa_decode_paged",
+    "fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_varlen_strided", "fa_bwd", "fa_bwd_workspace_bytes",
+    "attention_bwd", "fa_decode", "fa_decode_paged",
     "fa_decode_workspace_bytes", "fa_status_string", "fa_last_error", "fa_abi_version", "attention",
     "attention_varlen", "flash_attn_func", "flash_attn_varlen_func", "decode", "decode_paged", "dtype_code",
 ]
@@ -90,6 +93,10 @@ def load_library():
     lib.fa_fwd_strided.restype = i
     lib.fa_fwd_varlen_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_varlen_strided.restype = i
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_bwd_workspace_bytes.argtypes = [i, i, i]
+    lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
     lib.fa_decode.restype = i
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, i, i, vp]
@@ -156,6 +163,17 @@ def fa_fwd_varlen_strided(q, k, v, o, lse, strides, cu_seqlens_q, cu_seqlens_k, 
     return load_library().fa_fwd_varlen_strided(q, k, v, o, lse, ctypes.cast(arr, ctypes.c_void_p), cu_seqlens_q,
                                                 cu_seqlens_k, B, Hq, Hkv, total_q, total_k, max_seqlen_q, d, scale,
                                                 causal, dtype, stream)
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+           dtype, stream) -> int:
+    """Call the C ``fa_bwd`` with integer device addresses; returns the status."""
+    return load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk,
+                                 d, scale, causal, dtype, stream)
+
+
+def fa_bwd_workspace_bytes(B, Hq, Nq) -> int:
+    return load_library().fa_bwd_workspace_bytes(B, Hq, Nq)
 
 
 def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, workspace_bytes,
@@ -339,6 +357,43 @@ def flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: in
     o, lse = attention_varlen(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1), cu_seqlens_q, cu_seqlens_k,
                               max_seqlen_q, causal=causal, scale=softmax_scale, out=out.transpose(0, 1))
     return (out, lse) if return_lse else out
+
+
+def attention_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, dq=None, dk=None,
+                  dv=None, workspace=None):
+    """dQ, dK, dV for the forward attention(q, k, v) whose output o and LSE
+    lse are given, and an upstream gradient dout of o. q, o, dout
+    [B,Hq,Nq,d], k/v [B,Hkv,Nk,d], lse [B,Hq,Nq] fp32, all contiguous."""
+    _check_tensor("q", q, 4)
+    dev = q.device
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tensor(name, t, 4, dev)
+    _check_tensor("lse", lse, 3, dev)
+    if any(t.dtype != q.dtype for t in (k, v, o, dout)) or lse.dtype != torch.float32:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "q, k, v, o, dout must share a dtype and lse be float32")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk_ = k.shape
+    if ((Bk, dk_) != (B, d) or tuple(v.shape) != tuple(k.shape) or tuple(o.shape) != tuple(q.shape)
+            or tuple(dout.shape) != tuple(q.shape) or tuple(lse.shape) != (B, Hq, Nq)):
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "shape mismatch between q, k, v, o, lse and dout")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor(name, t, 4, dev)
+        if tuple(t.shape) != tuple(ref.shape) or t.dtype != ref.dtype:
+            raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must match the shape and dtype of its input")
+    need = fa_bwd_workspace_bytes(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        st = fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                    _ptr(workspace), workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d,
+                    float(scale), int(bool(causal)), dtype_code(q.dtype), _stream(dev))
+    _raise_for(st)
+    return dq, dk, dv
 
 
 def decode(q, k_cache, v_cache, seqlens, scale: float | None = None, num_splits: int = 0,

@@ -14,6 +14,7 @@
 #include <mutex>
 #include <string>
 
+#include "fa_bwd_launch.h"
 #include "fa_launch.h"
 
 namespace {
@@ -358,6 +359,62 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
   return decode_impl("fa_decode_paged", q, k_pages, v_pages, block_table, seqlens, o, lse, workspace,
                      workspace_bytes, B, Hq, Hkv, (int)Lcap, d, scale, num_splits, dtype, stream, cb, page_size,
                      max_pages, num_pages);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq) {
+  size_t n;
+  if (B <= 0 || Hq <= 0 || Nq <= 0 || !mul_bytes(n, {B, Hq, Nq, 4})) return 0;
+  return (n + 255) & ~(size_t)255;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                 int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
+    return fail(FA_ERR_INVALID_ARG, "fa_bwd: q, k, v, o, lse, dout, dq, dk, dv and workspace must be non-null");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(FA_ERR_INVALID_ARG, "fa_bwd: q, k, v, o, dout, dq, dk and dv must be 16-byte aligned");
+  if (!aligned(lse, 4) || !aligned(workspace, 256))
+    return fail(FA_ERR_INVALID_ARG, "fa_bwd: lse must be 4-byte and workspace 256-byte aligned");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0)
+    return fail(FA_ERR_INVALID_ARG, "fa_bwd: sizes must be positive (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d)", B, Hq, Hkv,
+                Nq, Nk, d);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "fa_bwd: causal must be 0 or 1");
+  fa_status st = check_common(d, dtype, scale, Hq, Hkv);
+  if (st != FA_OK) return st;
+  if (causal && Nq > Nk)
+    return fail(FA_ERR_INVALID_ARG, "fa_bwd: causal attention needs Nq <= Nk (Nq=%d Nk=%d)", Nq, Nk);
+  size_t qb, kb, lb;
+  if (!mul_bytes(qb, {B, Hq, Nq, d, 2}) || !mul_bytes(kb, {B, Hkv, Nk, d, 2}) || !mul_bytes(lb, {B, Hq, Nq, 4}))
+    return fail(FA_ERR_INVALID_ARG, "fa_bwd: tensor sizes overflow");
+  const size_t need = fa_bwd_workspace_bytes(B, Hq, Nq);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARG, "fa_bwd: workspace too small: %zu bytes given, %zu needed", workspace_bytes, need);
+  if ((long long)((Nq + fa::kBwdQueryRows - 1) / fa::kBwdQueryRows) * B * Hq > 0x7fffffffLL ||
+      (long long)((Nk + fa::kBwdKeyRows - 1) / fa::kBwdKeyRows) * B * Hkv > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "fa_bwd: grid too large");
+  // outputs and the workspace may overlap nothing else
+  const void* ins[6] = {q, k, v, o, lse, dout};
+  const size_t in_b[6] = {qb, kb, kb, qb, lb, qb};
+  void* outs[4] = {dq, dk, dv, workspace};
+  const size_t out_b[4] = {qb, kb, kb, need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(outs[i], out_b[i], ins[j], in_b[j]))
+        return fail(FA_ERR_INVALID_ARG, "fa_bwd: an output or the workspace overlaps an input");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], out_b[i], outs[j], out_b[j]))
+        return fail(FA_ERR_INVALID_ARG, "fa_bwd: two outputs (or an output and the workspace) overlap");
+  }
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, static_cast<float*>(workspace), B, Hq, Hkv, Nq, Nk, d,
+                scale, causal, dtype};
+  hipError_t e = fa::launch_bwd(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_bwd launch: %s", hipGetErrorString(e));
+  return FA_OK;
 }
 
 }  // extern "C"

@@ -166,6 +166,46 @@ fa_status fa_fwd_varlen_strided(const void* q, const void* k, const void* v, voi
                                 int dtype, void* stream);
 
 /*
+ * fa_bwd_workspace_bytes - bytes of device workspace fa_bwd needs (one fp32
+ * per query row, rounded up to 256). Returns 0 if the sizes are invalid.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq);
+
+/*
+ * fa_bwd - gradients dQ, dK, dV of the prefill forward for an upstream
+ * gradient dO of its output.
+ *
+ * Source: "Flash Attention: Revolutionizing Transformer Efficiency"
+ * (unite.ai): the forward is the standard-attention definition of that page
+ * (as fa_fwd); its "Enter Flash Attention" list (point 2) has the backward
+ * pass recompute the parts of the attention matrix it needs rather than store
+ * it, and its FlashAttention-2 section (point 2) names the backward pass as
+ * the part brought close to forward speed. The gradients are those of the
+ * forward definition (the chain rule; the pages give no formulas):
+ *     P = exp(scale Q K^T - LSE) (0 where masked),  dV = P^T dO,
+ *     dS = P * (dO V^T - rowsum(dO * O)),  dQ = scale dS K,  dK = scale dS^T Q.
+ * A kv-head's dK and dV sum the contributions of every q-head that reads it.
+ *
+ *   q, o, dout  [B, Hq, Nq, d]  inputs, dtype; o is fa_fwd's output for q, k, v
+ *   k, v        [B, Hkv, Nk, d] inputs, dtype
+ *   lse         [B, Hq, Nq] fp32 input, fa_fwd's LSE for the same call
+ *   dq          [B, Hq, Nq, d]  output, dtype
+ *   dk, dv      [B, Hkv, Nk, d] output, dtype
+ *   workspace, workspace_bytes: device scratch of at least
+ *               fa_bwd_workspace_bytes(B, Hq, Nq) bytes, 256-byte aligned,
+ *               owned by the caller; contents on entry are ignored.
+ *   d, scale, causal, dtype: as in fa_fwd (the same values as the forward).
+ *
+ * All tensors contiguous row-major. Outputs and the workspace must not
+ * overlap each other or any input. The result is deterministic (no atomics).
+ * Returns FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                 const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                 int causal, int dtype, void* stream);
+
+/*
  * fa_decode_workspace_bytes - bytes of device workspace fa_decode needs for
  * these sizes and this `num_splits` (0 = the library's choice). Returns 0 if
  * the sizes are invalid. The workspace holds per-split partial outputs and

@@ -29,8 +29,9 @@ def test_library_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_varlen_strided", "fa_decode", "fa_decode_paged",
-            "fa_decode_workspace_bytes", "fa_status_string", "fa_last_error"} <= set(names)
+    assert {"fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_varlen_strided", "fa_bwd", "fa_bwd_workspace_bytes",
+            "fa_decode", "fa_decode_paged", "fa_decode_workspace_bytes", "fa_status_string",
+            "fa_last_error"} <= set(names)
     raw = ctypes.CDLL(fa.lib_path())
     for n in names:
         assert hasattr(raw, n), f"{n} declared in fa.h but not exported"
@@ -209,6 +210,46 @@ def test_fwd_strided_needs_its_stride_count():
     with pytest.raises(ValueError):
         fa.fa_fwd_varlen_strided(FAKE, FAKE, FAKE, FAKE, None, [64] * 7, FAKE, FAKE, 1, 1, 1, 8, 8, 8, 64, 0.1, 0,
                                  0, None)
+
+
+def bwd(**kw):
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, lse=FAKE + 0x400000,
+             do=FAKE + 0x500000, dq=FAKE + 0x600000, dk=FAKE + 0x700000, dv=FAKE + 0x800000,
+             ws=FAKE + 0x900000, ws_bytes=1 << 20, B=1, Hq=8, Hkv=2, Nq=128, Nk=128, d=64, scale=0.125,
+             causal=1, dtype=0, stream=None)
+    a.update(kw)
+    return fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["ws"],
+                     a["ws_bytes"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                     a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(do=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=FAKE + 0x800008), fa.FA_ERR_INVALID_ARG),     # misaligned
+    (dict(ws=FAKE + 0x900010), fa.FA_ERR_INVALID_ARG),     # workspace not 256-byte aligned
+    (dict(ws_bytes=128 * 8 * 4 - 4), fa.FA_ERR_INVALID_ARG),  # workspace too small
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=1, Nq=200, Nk=128), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=3), fa.FA_ERR_UNSUPPORTED),
+    (dict(dq=FAKE + 0x1000), fa.FA_ERR_INVALID_ARG),        # dq inside q
+    (dict(dk=FAKE + 0x800000), fa.FA_ERR_INVALID_ARG),      # dk == dv
+    (dict(ws=FAKE + 0x600000), fa.FA_ERR_INVALID_ARG),      # workspace inside dq
+    (dict(dv=FAKE + 0x400000), fa.FA_ERR_INVALID_ARG),      # dv over lse
+])
+def test_bwd_rejects_before_launch(kw, status):
+    st = bwd(**kw)
+    assert st == status, (st, fa.fa_last_error())
+    assert fa.fa_last_error() != ""
+
+
+def test_bwd_workspace_bytes():
+    assert fa.fa_bwd_workspace_bytes(1, 32, 8192) == 32 * 8192 * 4
+    assert fa.fa_bwd_workspace_bytes(2, 3, 5) == 256
+    assert fa.fa_bwd_workspace_bytes(0, 3, 5) == 0
 
 
 def dec_paged(**kw):
