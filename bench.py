@@ -54,6 +54,7 @@ KERNEL_SOURCES = [os.path.join(CSRC, f)
 # The device code behind each measured kernel (its counter summary records these).
 FWD_D128_SOURCES = ("fa_fwd_d128.hip", "fa_tile.h", "fa_launch.h")
 DECODE_SOURCES = ("fa_decode.hip", "fa_tile.h", "fa_launch.h")
+BWD_SOURCES = ("fa_bwd.hip", "fa_bwd_launch.h", "fa_tile.h", "fa_launch.h")
 
 
 def log(*a):
@@ -486,8 +487,9 @@ def main():
         out["prefill"] = {"workload": f"{wl} causal={causal}", "ms_mean": round(t_ms, 4),
                           "ms_min": round(float(np.min(per[i])), 4), "tflops": round(tflops, 2),
                           "frac_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS, 4)}
-        prof = cfg if cfg in ("llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd", "llama3_8b_gqa_n8192_bwd") else pname
-        traffic = counter_traffic(f"fa_fwd_{prof}_counters.md") if causal else None
+        prof = cfg if cfg in ("llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd") else pname
+        kind = "bwd" if cfg.endswith("_bwd") else "fwd"
+        traffic = counter_traffic(f"fa_{kind}_{prof}_counters.md") if causal else None
         out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
                            "algorithmic_bytes": pre.bytes, "flops_per_launch": pre.flops}

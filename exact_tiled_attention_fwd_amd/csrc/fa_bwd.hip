@@ -225,16 +225,25 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(
     const float* l2 = reinterpret_cast<const float*>(qt + 2 * TILE);
     const float* dl = l2 + kTileRows;
     const int i0 = (t_first + it % per_head) * kTileRows;
+    // S = Q K^T and dP = dO V^T for both 32-row blocks (four independent chains)
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[qb][r] = dp[qb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        s[qb] = mfma32<DT>(row_op<D>(qt, 32 * qb + (lane & 31), 2 * ks + half), kop[ks], s[qb]);
+        dp[qb] = mfma32<DT>(row_op<D>(dot, 32 * qb + (lane & 31), 2 * ks + half), vop[ks], dp[qb]);
+      }
+    // Masking is needed only where this wave's keys reach past the tile's
+    // first row (causal diagonal) or past Nk (ragged key tile).
+    const int wk0 = kt0 + 32 * wave;
+    const bool need_mask = (wk0 + 31 >= Nk) || (CAUSAL && wk0 + 31 > i0 + off);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32<DT>(row_op<D>(qt, 32 * qb + (lane & 31), 2 * ks + half), kop[ks], s);
-        dp = mfma32<DT>(row_op<D>(dot, 32 * qb + (lane & 31), 2 * ks + half), vop[ks], dp);
-      }
       // P and dS; register r holds query row 32 qb + acc_key(r, half).
       uint32_t pk[8], dsk[8];
 #pragma unroll
@@ -246,16 +255,21 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * m + e;
-          float x = exp2_fast(__builtin_fmaf(s[r], c2, -L[e]));
-          if (key >= Nk || (CAUSAL && key > i0 + rl0 + e + off)) x = 0.f;
+          float x = exp2_fast(__builtin_fmaf(s[qb][r], c2, -L[e]));
+          if (need_mask) {
+            const bool hide = (key >= Nk) | (CAUSAL & (key > i0 + rl0 + e + off));
+            x = hide ? 0.f : x;
+          }
           p[e] = x;
-          ds[e] = x * (dp[r] - Dv[e]);
+          ds[e] = x * (dp[qb][r] - Dv[e]);
         }
         pk[2 * m] = pack2<DT>(p[0], p[1]);
         pk[2 * m + 1] = pack2<DT>(p[2], p[3]);
         dsk[2 * m] = pack2<DT>(ds[0], ds[1]);
         dsk[2 * m + 1] = pack2<DT>(ds[2], ds[3]);
       }
+      // dV^T += dO^T P, dK^T += Q^T dS (the next block's exponentials can
+      // overlap these)
 #pragma unroll
       for (int G = 0; G < 2; ++G) {
         const u32x4 bp = {pk[4 * G], pk[4 * G + 1], pk[4 * G + 2], pk[4 * G + 3]};
@@ -305,7 +319,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dq_kernel(
   const int b = bh / Hq, h = bh % Hq, g = h / (Hq / Hkv);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
   const int q0 = qt * kBwdQueryRows;
-  const int qrow = q0 + 32 * wave + (lane & 31);  // this lane's query column
+  const int q0w = q0 + 32 * wave;                  // first query row of this wave
+  const int qrow = q0w + (lane & 31);             // this lane's query column
   const int off = Nk - Nq;
   const size_t qo = (size_t)bh * Nq;
   const size_t kvo = ((size_t)b * Hkv + g) * Nk * D;
@@ -351,27 +366,37 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dq_kernel(
     if (j + 1 < n_kv) fetch(j + 1);
     const char* kt = smem + (j & 1) * 2 * TILE;
     const char* vt = kt + TILE;
+    // S^T = K Q^T and dP^T = V dO^T for both 32-key blocks (four chains)
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = mfma32<DT>(row_op<D>(kt, 32 * kb + (lane & 31), 2 * ks + half), qop[ks], s[kb]);
+        dp[kb] = mfma32<DT>(row_op<D>(vt, 32 * kb + (lane & 31), 2 * ks + half), dop[ks], dp[kb]);
+      }
+    // masking only on the causal diagonal or a ragged last tile
+    const bool need_mask = (j * kTileRows + kTileRows > Nk) || (CAUSAL && j * kTileRows + kTileRows - 1 > q0w + off);
     uint32_t dsk[2][8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32<DT>(row_op<D>(kt, 32 * kb + (lane & 31), 2 * ks + half), qop[ks], s);
-        dp = mfma32<DT>(row_op<D>(vt, 32 * kb + (lane & 31), 2 * ks + half), dop[ks], dp);
-      }
       // register r holds key j*64 + 32 kb + acc_key(r, half) of this lane's query
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float ds[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int key = j * kTileRows + 32 * kb + acc_key(r + u, half);
-          float x = exp2_fast(__builtin_fmaf(s[r + u], c2, -l2));
-          if (key >= Nk || (CAUSAL && key > qrow + off)) x = 0.f;
-          ds[u] = x * (dp[r + u] - dl);
+          float x = exp2_fast(__builtin_fmaf(s[kb][r + u], c2, -l2));
+          if (need_mask) {
+            const int key = j * kTileRows + 32 * kb + acc_key(r + u, half);
+            const bool hide = (key >= Nk) | (CAUSAL & (key > qrow + off));
+            x = hide ? 0.f : x;
+          }
+          ds[u] = x * (dp[kb][r + u] - dl);
         }
         dsk[kb][r >> 1] = pack2<DT>(ds[0], ds[1]);
       }
