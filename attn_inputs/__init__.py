@@ -26,7 +26,8 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 __all__ = [
-    "BF16", "FP16", "Q_ID", "K_ID", "V_ID", "DO_ID", "grad_output",
+    "BF16", "FP16", "FP8", "Q_ID", "K_ID", "V_ID", "DO_ID", "grad_output", "fp8_decode", "fp8_encode",
+    "fp8_quantize", "prefill_inputs_fp8", "fp8_to_f64",
     "round_to_bits", "bits_to_f64", "slab", "prefill_inputs",
     "decode_lengths", "decode_inputs", "paged_layout", "varlen_inputs", "sample_rows", "CONFIGS",
 ]
@@ -87,6 +88,75 @@ def bits_to_f64(bits: np.ndarray, dtype: str) -> np.ndarray:
     if dtype != BF16:
         raise ValueError(f"unknown dtype {dtype!r}")
     return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+# ------------------------------------------------------------------ FP8 (e4m3)
+# OCP 8-bit float E4M3 ("fn": no infinities): 1 sign, 4 exponent (bias 7), 3
+# mantissa bits; exponent field 0 is subnormal (m * 2^-9); 0x7F / 0xFF is NaN;
+# the largest finite value is 448 (0x7E).
+FP8 = "fp8e4m3"
+FP8_MAX = 448.0
+
+
+def fp8_decode(codes: np.ndarray) -> np.ndarray:
+    """E4M3 codes (uint8) -> float64, exactly."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    out = sign * mag
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+_FP8_POS = fp8_decode(np.arange(0x7F, dtype=np.uint8))  # codes 0..0x7E, increasing
+
+
+def fp8_encode(x: np.ndarray) -> np.ndarray:
+    """float -> nearest E4M3 code, ties to the even code; |x| > 448 saturates
+    to 448 (inputs are scaled into range first, so this does not occur)."""
+    x = np.asarray(x, np.float64)
+    a = np.minimum(np.abs(x), FP8_MAX)
+    hi = np.clip(np.searchsorted(_FP8_POS, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    dlo, dhi = a - _FP8_POS[lo], _FP8_POS[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = pick.astype(np.uint8)
+    return np.where((x < 0) & (code != 0), code | 0x80, code).astype(np.uint8)
+
+
+def fp8_quantize(x: np.ndarray):
+    """One slab -> (codes, descale): descale is the power of two that brings
+    max|x| to at most 448, so x / descale is exact before rounding and the
+    value a code stands for is fp8_decode(code) * descale."""
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    e = int(np.ceil(np.log2(amax / FP8_MAX))) if amax > 0 else 0
+    descale = float(2.0 ** e)
+    return fp8_encode(np.asarray(x, np.float64) / descale), descale
+
+
+def prefill_inputs_fp8(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, Nk: int | None = None) -> dict:
+    """Q [B,Hq,N,d], K/V [B,Hkv,Nk,d] as E4M3 codes (uint8) with one float32
+    descale per (batch, head) slab ([B,Hq] for q, [B,Hkv] for k and v). The
+    underlying draws are the float32 N(0,1) values of ``slab`` (before any
+    16-bit rounding), quantized slab by slab."""
+    Nk = N if Nk is None else Nk
+    out = {}
+    for name, tid, H, n in (("q", Q_ID, Hq, N), ("k", K_ID, Hkv, Nk), ("v", V_ID, Hkv, Nk)):
+        codes = np.empty((B, H, n, d), np.uint8)
+        ds = np.empty((B, H), np.float32)
+        for b in range(B):
+            for h in range(H):
+                raw = np.random.default_rng([seed, tid, b, h]).standard_normal(size=(n, d), dtype=np.float32)
+                codes[b, h], ds[b, h] = fp8_quantize(raw)
+        out[name], out[name + "_descale"] = codes, ds
+    out["dtype"] = FP8
+    return out
+
+
+def fp8_to_f64(codes: np.ndarray, descale: np.ndarray) -> np.ndarray:
+    """Codes [B,H,N,d] and descales [B,H] -> the float64 values they stand for."""
+    return fp8_decode(codes) * np.asarray(descale, np.float64)[:, :, None, None]
 
 
 def slab(seed: int, tensor_id: int, b: int, head: int, n: int, d: int, dtype: str) -> np.ndarray:

@@ -46,6 +46,7 @@ import numpy as np  # noqa: E402
 import attn_inputs as ai  # noqa: E402
 
 MFMA_PEAK_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+MFMA_PEAK_FP8_TFLOPS = 5033.2  # dense FP8 MFMA: twice the 16-bit rate
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "exact_tiled_attention_fwd_amd", "csrc")
@@ -55,6 +56,7 @@ KERNEL_SOURCES = [os.path.join(CSRC, f)
 FWD_D128_SOURCES = ("fa_fwd_d128.hip", "fa_tile.h", "fa_launch.h")
 DECODE_SOURCES = ("fa_decode.hip", "fa_tile.h", "fa_launch.h")
 BWD_SOURCES = ("fa_bwd.hip", "fa_bwd_launch.h", "fa_tile.h", "fa_launch.h")
+FP8_SOURCES = ("fa_fwd_fp8.hip", "fa_fp8_launch.h", "fa_tile.h", "fa_launch.h")
 
 
 def log(*a):
@@ -144,6 +146,32 @@ class Prefill:
 
     def __call__(self):
         self.fa.attention(self.q, self.k, self.v, causal=self.causal, out=self.o, lse=self.lse)
+
+
+class PrefillFp8:
+    """The Llama-3 layer with E4M3 inputs (per-slab power-of-two descales);
+    output bf16. Same FLOP count as the 16-bit layer; the FP8 matrix-core
+    peak is twice the 16-bit one."""
+
+    def __init__(self, fa, name, causal):
+        import torch
+        c = ai.CONFIGS[name]
+        self.fa, self.causal = fa, causal
+        B, Hq, Hkv, N, d = c["B"], c["Hq"], c["Hkv"], c["N"], c["d"]
+        t0 = time.time()
+        x = ai.prefill_inputs_fp8(c["seed"], B, Hq, Hkv, N, d)
+        self.q, self.k, self.v = (torch.from_numpy(x[n]).cuda() for n in "qkv")
+        self.ds = [torch.from_numpy(x[n + "_descale"]).cuda() for n in "qkv"]
+        del x
+        self.o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.empty((B, Hq, N), dtype=torch.float32, device="cuda")
+        self.flops = prefill_flops(B, Hq, N, N, d, causal)
+        # q, k, v one byte per element; o bf16; lse fp32
+        self.bytes = (B * Hq * N * d + 2 * B * Hkv * N * d) + 2 * B * Hq * N * d + 4 * B * Hq * N
+        log(f"[bench] {name} fp8 causal={causal}: inputs ready in {time.time() - t0:.1f}s")
+
+    def __call__(self):
+        self.fa.attention_fp8(self.q, self.k, self.v, *self.ds, causal=self.causal, out=self.o, lse=self.lse)
 
 
 class Backward:
@@ -300,26 +328,33 @@ def cpu_cores_used():
     return cores
 
 
-def cpu_baseline_prefill(name="llama3_8b_gqa_n8192", heads=32):
+def cpu_baseline_prefill(name="llama3_8b_gqa_n8192", heads=32, fp8=False):
     """The oracle on `heads` full heads of the prefill workload (all query rows,
-    all keys, causal): TFLOP/s by the same FLOP convention as the GPU."""
+    all keys, causal): TFLOP/s by the same FLOP convention as the GPU. With
+    fp8, the inputs are the values the E4M3 workload's codes stand for."""
     import oracle
     c = ai.CONFIGS[name]
     N, d, dt, grp = c["N"], c["d"], c["dtype"], c["Hq"] // c["Hkv"]
     scale = 1.0 / math.sqrt(d)
+    x8 = ai.prefill_inputs_fp8(c["seed"], 1, c["Hq"], c["Hkv"], N, d) if fp8 else None
     elapsed = 0.0
     for h in range(heads):
         g = h // grp
-        q = ai.bits_to_f64(ai.slab(c["seed"], ai.Q_ID, 0, h, N, d, dt), dt)
-        k = ai.bits_to_f64(ai.slab(c["seed"], ai.K_ID, 0, g, N, d, dt), dt)
-        v = ai.bits_to_f64(ai.slab(c["seed"], ai.V_ID, 0, g, N, d, dt), dt)
+        if fp8:
+            q = ai.fp8_decode(x8["q"][0, h]) * float(x8["q_descale"][0, h])
+            k = ai.fp8_decode(x8["k"][0, g]) * float(x8["k_descale"][0, g])
+            v = ai.fp8_decode(x8["v"][0, g]) * float(x8["v_descale"][0, g])
+        else:
+            q = ai.bits_to_f64(ai.slab(c["seed"], ai.Q_ID, 0, h, N, d, dt), dt)
+            k = ai.bits_to_f64(ai.slab(c["seed"], ai.K_ID, 0, g, N, d, dt), dt)
+            v = ai.bits_to_f64(ai.slab(c["seed"], ai.V_ID, 0, g, N, d, dt), dt)
         t0 = time.perf_counter()
         oracle.attention_head(q, k, v, scale, causal=True)
         elapsed += time.perf_counter() - t0
     flops = prefill_flops(1, heads, N, N, d, True)
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cpu_cores_used(), "kind": "oracle",
-            "sample": f"{heads} of 32 q-heads of the N=8192 causal layer, all 8192 query rows each "
-                      f"(float64 NumPy, score matrix materialised); {elapsed:.1f}s"}
+            "sample": f"{heads} of 32 q-heads of the N=8192 causal layer{' (E4M3 inputs, dequantized)' if fp8 else ''}, "
+                      f"all 8192 query rows each (float64 NumPy, score matrix materialised); {elapsed:.1f}s"}
 
 
 def cpu_baseline_backward(name="llama3_8b_gqa_n8192", heads=4):
@@ -452,15 +487,17 @@ def main():
     cfg = args.config
     run_prefill = cfg in ("default", "tiny_mha_n128", "mha_n4096_fp16", "mha_n4096_fp16_causal", "llama3_8b_gqa_n8192",
                           "llama3_8b_gqa_n131072", "llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd",
-                          "llama3_8b_gqa_n8192_bwd")
+                          "llama3_8b_gqa_n8192_bwd", "llama3_8b_gqa_n8192_fp8")
     run_decode = cfg in ("default", "decode_32seq_gqa", "decode_32seq_gqa_paged")
     paged = cfg == "decode_32seq_gqa_paged"
     if not (run_prefill or run_decode):
         raise SystemExit(f"unknown --config {cfg}")
-    pname = ("llama3_8b_gqa_n8192" if cfg in ("default", "llama3_8b_gqa_n8192_bshd", "llama3_8b_gqa_n8192_bwd")
+    pname = ("llama3_8b_gqa_n8192" if cfg in ("default", "llama3_8b_gqa_n8192_bshd", "llama3_8b_gqa_n8192_bwd",
+                                              "llama3_8b_gqa_n8192_fp8")
              else cfg.replace("_causal", ""))
     causal = cfg in ("default", "llama3_8b_gqa_n8192", "llama3_8b_gqa_n131072", "mha_n4096_fp16_causal",
-                     "llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd", "llama3_8b_gqa_n8192_bwd")
+                     "llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd", "llama3_8b_gqa_n8192_bwd",
+                     "llama3_8b_gqa_n8192_fp8")
     parts = []
     pre = dec = None
     if run_prefill:
@@ -468,6 +505,8 @@ def main():
             pre = PrefillVarlen(fa)
         elif cfg.endswith("_bwd"):
             pre = Backward(fa, pname, causal)
+        elif cfg.endswith("_fp8"):
+            pre = PrefillFp8(fa, pname, causal)
         else:
             pre = Prefill(fa, pname, causal, layout="bshd" if cfg.endswith("_bshd") else "bhnd")
         parts.append(pre)
@@ -483,15 +522,17 @@ def main():
         t_ms = float(np.mean(per[i]))
         tflops = pre.flops / (t_ms * 1e-3) / 1e12
         out.update(value=round(tflops, 2), unit="TFLOP/s")
-        wl = cfg if cfg in ("llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd", "llama3_8b_gqa_n8192_bwd") else pname
+        wl = cfg if cfg in ("llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd", "llama3_8b_gqa_n8192_bwd",
+                            "llama3_8b_gqa_n8192_fp8") else pname
+        peak = MFMA_PEAK_FP8_TFLOPS if cfg.endswith("_fp8") else MFMA_PEAK_TFLOPS
         out["prefill"] = {"workload": f"{wl} causal={causal}", "ms_mean": round(t_ms, 4),
                           "ms_min": round(float(np.min(per[i])), 4), "tflops": round(tflops, 2),
-                          "frac_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS, 4)}
-        prof = cfg if cfg in ("llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd") else pname
+                          "frac_mfma_peak": round(tflops / peak, 4)}
+        prof = cfg if cfg in ("llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd", "llama3_8b_gqa_n8192_fp8") else pname
         kind = "bwd" if cfg.endswith("_bwd") else "fwd"
         traffic = counter_traffic(f"fa_{kind}_{prof}_counters.md") if causal else None
-        out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS,
-                           "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": traffic,
+        out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                           "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic,
                            "algorithmic_bytes": pre.bytes, "flops_per_launch": pre.flops}
         i += 1
     if dec is not None:
@@ -506,8 +547,10 @@ def main():
             out.update(value=round(gbs, 1), unit="GB/s", roofline=droof)
     out.update({
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if cfg != "mha_n4096_fp16" and cfg != "mha_n4096_fp16_causal" else "fp16",
-        "data": "synthetic: seeded N(0,1) rounded to bf16/fp16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": ("fp8e4m3" if cfg.endswith("_fp8") else "bf16" if cfg not in ("mha_n4096_fp16", "mha_n4096_fp16_causal")
+                  else "fp16"),
+        "data": ("synthetic: seeded N(0,1) quantized to E4M3 per (batch, head) slab" if cfg.endswith("_fp8")
+                 else "synthetic: seeded N(0,1) rounded to bf16/fp16"),
         "config": {"workload": "llama3_8b_gqa_n8192 prefill (B=1,Hq=32,Hkv=8,N=8192,d=128,causal,bf16) + decode_32seq_gqa (32 seq x 1 token, Hq=32,Hkv=8,d=128,bf16, L~U[1024,32768])"
                    if cfg == "default" else cfg,
                    "kernel_source_sha256": kernel_source_hash()},
@@ -517,6 +560,8 @@ def main():
             out["cpu_baseline"] = cpu_baseline_varlen()
         elif cfg == "llama3_8b_gqa_n8192_bwd":
             out["cpu_baseline"] = cpu_baseline_backward()
+        elif cfg == "llama3_8b_gqa_n8192_fp8":
+            out["cpu_baseline"] = cpu_baseline_prefill(fp8=True)
         elif pre is not None and pname == "llama3_8b_gqa_n8192":
             out["cpu_baseline"] = cpu_baseline_prefill()
             if dec is not None:

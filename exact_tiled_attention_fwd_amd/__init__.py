@@ -6,7 +6,7 @@ runs in the HIP kernels of that library; this module only marshals arguments.
 PyTorch supplies device memory and the current stream.
 
 Raw entry points, same names and argument order as the C header:
-    fa_fwd, fa_fwd_strided, fa_fwd_varlen, fa_fwd_varlen_strided, fa_bwd,
+    fa_fwd, fa_fwd_strided, fa_fwd_varlen, fa_fwd_varlen_strided, fa_fwd_fp8, fa_bwd,
     fa_bwd_workspace_bytes, fa_decode, fa_decode_paged,
     fa_decode_workspace_bytes, fa_status_string, fa_last_error, fa_abi_version
 Tensor-level helpers:
@@ -20,6 +20,8 @@ Tensor-level helpers:
     flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                            max_seqlen_k, dropout_p=0.0, softmax_scale=None,
                            causal=False) -> o, for q [total_q,Hq,d]
+    attention_fp8(q, k, v, q_descale, k_descale, v_descale, causal=False,
+                  scale=None) -> (o bf16, lse), E4M3 inputs [B,H,N,128]
     attention_bwd(q, k, v, o, lse, dout, causal=False, scale=None)
         -> (dq, dk, dv), for the contiguous layouts of attention()
     decode(q, k_cache, v_cache, seqlens, scale=None, num_splits=0) -> (o, lse)
@@ -40,7 +42,8 @@ import torch  # loads the HIP runtime that libfa.so then binds to
 __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
     "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FAError", "lib_path", "load_library",
-    "fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_varlen_strided", "fa_bwd", "fa_bwd_workspace_bytes",
+    "fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_varlen_strided", "fa_fwd_fp8", "attention_fp8", "fa_bwd",
+    "fa_bwd_workspace_bytes",
     "attention_bwd", "fa_decode", "fa_decode_paged",
     "fa_decode_workspace_bytes", "fa_status_string", "fa_last_error", "fa_abi_version", "attention",
     "attention_varlen", "flash_attn_func", "flash_attn_varlen_func", "decode", "decode_paged", "dtype_code",
@@ -93,6 +96,8 @@ def load_library():
     lib.fa_fwd_strided.restype = i
     lib.fa_fwd_varlen_strided.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp]
     lib.fa_fwd_varlen_strided.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, i, vp]
     lib.fa_bwd.restype = i
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i]
@@ -163,6 +168,13 @@ def fa_fwd_varlen_strided(q, k, v, o, lse, strides, cu_seqlens_q, cu_seqlens_k, 
     return load_library().fa_fwd_varlen_strided(q, k, v, o, lse, ctypes.cast(arr, ctypes.c_void_p), cu_seqlens_q,
                                                 cu_seqlens_k, B, Hq, Hkv, total_q, total_k, max_seqlen_q, d, scale,
                                                 causal, dtype, stream)
+
+
+def fa_fwd_fp8(q, k, v, o, lse, q_descale, k_descale, v_descale, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+               stream) -> int:
+    """Call the C ``fa_fwd_fp8`` with integer device addresses; returns the status."""
+    return load_library().fa_fwd_fp8(q, k, v, o, lse, q_descale, k_descale, v_descale, B, Hq, Hkv, Nq, Nk, d, scale,
+                                     causal, stream)
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d, scale, causal,
@@ -357,6 +369,44 @@ def flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: in
     o, lse = attention_varlen(q.transpose(0, 1), k.transpose(0, 1), v.transpose(0, 1), cu_seqlens_q, cu_seqlens_k,
                               max_seqlen_q, causal=causal, scale=softmax_scale, out=out.transpose(0, 1))
     return (out, lse) if return_lse else out
+
+
+def attention_fp8(q, k, v, q_descale, k_descale, v_descale, causal: bool = False, scale: float | None = None,
+                  out=None, lse=None):
+    """O (bf16), LSE for E4M3 inputs: q [B,Hq,Nq,128], k/v [B,Hkv,Nk,128] as
+    torch.uint8 or torch.float8_e4m3fn (contiguous), descales float32
+    [B,Hq] / [B,Hkv]: element x of a slab stands for x * descale."""
+    def u8(name, t):
+        _check_tensor(name, t, 4, q.device if name != "q" else None)
+        if t.dtype == getattr(torch, "float8_e4m3fn", None):
+            return t.view(torch.uint8)
+        if t.dtype != torch.uint8:
+            raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must be uint8 or float8_e4m3fn")
+        return t
+    q8, k8, v8 = u8("q", q), u8("k", k), u8("v", v)
+    dev = q.device
+    B, Hq, Nq, d = q8.shape
+    Bk, Hkv, Nk, dk = k8.shape
+    if (Bk, dk) != (B, d) or tuple(v8.shape) != tuple(k8.shape):
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "shape mismatch between q, k and v")
+    for name, t, shape in (("q_descale", q_descale, (B, Hq)), ("k_descale", k_descale, (B, Hkv)),
+                           ("v_descale", v_descale, (B, Hkv))):
+        _check_tensor(name, t, 2, dev)
+        if t.dtype != torch.float32 or tuple(t.shape) != shape:
+            raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must be float32 of shape {shape}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    _check_tensor("out", out, 4, dev)
+    _check_tensor("lse", lse, 3, dev)
+    with torch.cuda.device(dev):
+        st = fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(out), _ptr(lse), _ptr(q_descale), _ptr(k_descale),
+                        _ptr(v_descale), B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _stream(dev))
+    _raise_for(st)
+    return out, lse
 
 
 def attention_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, dq=None, dk=None,

@@ -15,6 +15,7 @@
 #include <string>
 
 #include "fa_bwd_launch.h"
+#include "fa_fp8_launch.h"
 #include "fa_launch.h"
 
 namespace {
@@ -359,6 +360,46 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
   return decode_impl("fa_decode_paged", q, k_pages, v_pages, block_table, seqlens, o, lse, workspace,
                      workspace_bytes, B, Hq, Hkv, (int)Lcap, d, scale, num_splits, dtype, stream, cb, page_size,
                      max_pages, num_pages);
+}
+
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, const float* q_descale,
+                     const float* k_descale, const float* v_descale, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                     float scale, int causal, void* stream) {
+  g_last_error.clear();
+  if (!q || !k || !v || !o || !q_descale || !k_descale || !v_descale)
+    return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: q, k, v, o and the three descale arrays must be non-null");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+    return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: q, k, v and o must be 16-byte aligned");
+  if (!aligned(q_descale, 4) || !aligned(k_descale, 4) || !aligned(v_descale, 4) || (lse && !aligned(lse, 4)))
+    return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: descales and lse must be 4-byte aligned");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0)
+    return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: sizes must be positive (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d)", B, Hq,
+                Hkv, Nq, Nk, d);
+  if (d != 128) return fail(FA_ERR_UNSUPPORTED, "fa_fwd_fp8: head width d=%d is not 128", d);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: causal must be 0 or 1");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: scale must be finite and > 0 (got %g)", (double)scale);
+  if (Hq % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (causal && Nq > Nk)
+    return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: causal attention needs Nq <= Nk (Nq=%d Nk=%d)", Nq, Nk);
+  size_t qb, kb, ob, lb, dqb, dkb;
+  if (!mul_bytes(qb, {B, Hq, Nq, d}) || !mul_bytes(kb, {B, Hkv, Nk, d}) || !mul_bytes(ob, {B, Hq, Nq, d, 2}) ||
+      !mul_bytes(lb, {B, Hq, Nq, 4}) || !mul_bytes(dqb, {B, Hq, 4}) || !mul_bytes(dkb, {B, Hkv, 4}))
+    return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: tensor sizes overflow");
+  if ((long long)((Nq + fa::kFp8BlockRows - 1) / fa::kFp8BlockRows) * B * Hq > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "fa_fwd_fp8: grid too large");
+  if (overlap(o, ob, q, qb) || overlap(o, ob, k, kb) || overlap(o, ob, v, kb) || overlap(o, ob, q_descale, dqb) ||
+      overlap(o, ob, k_descale, dkb) || overlap(o, ob, v_descale, dkb))
+    return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: o overlaps an input");
+  if (lse && (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) || overlap(lse, lb, o, ob)))
+    return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: lse overlaps another tensor");
+  fa_status st = check_device();
+  if (st != FA_OK) return st;
+  fa::Fp8Args a{static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), o,
+                lse, q_descale, k_descale, v_descale, B, Hq, Hkv, Nq, Nk, scale, causal};
+  hipError_t e = fa::launch_fwd_fp8(a, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_fwd_fp8 launch: %s", hipGetErrorString(e));
+  return FA_OK;
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq) {

@@ -166,6 +166,37 @@ fa_status fa_fwd_varlen_strided(const void* q, const void* k, const void* v, voi
                                 int dtype, void* stream);
 
 /*
+ * fa_fwd_fp8 - prefill attention forward with 8-bit float inputs.
+ *
+ * Source: "Flash Attention: Revolutionizing Transformer Efficiency"
+ * (unite.ai), section "FlashAttention-3", point 2: computing in low-precision
+ * FP8 for speed (point 3 names a technique against quantization error without
+ * describing it; none is applied here). The operation is fa_fwd's on the
+ * values the 8-bit inputs stand for: element x of the (b, head) slab of q
+ * stands for x * q_descale[b, head], likewise k and v with their kv-head.
+ * The probabilities are rounded to FP8 for the second product (after scaling
+ * by 2^8, so that they use E4M3's normal range), which bounds the accuracy:
+ * about 4% relative error on O for nearly flat attention rows; the LSE is
+ * computed in fp32.
+ *
+ *   q          [B, Hq, Nq, 128]  input, OCP FP8 E4M3 bytes (no infinities;
+ *              0x7F/0xFF are NaN; largest finite 448)
+ *   k, v       [B, Hkv, Nk, 128] input, E4M3 bytes
+ *   o          [B, Hq, Nq, 128]  output, bf16
+ *   lse        [B, Hq, Nq] fp32 output or NULL
+ *   q_descale  [B, Hq] fp32, device memory; k_descale, v_descale [B, Hkv]
+ *   d          must be 128 (else FA_ERR_UNSUPPORTED)
+ *   scale, causal: as in fa_fwd (scale multiplies the dequantized Q K^T)
+ *
+ * Contiguous row-major tensors; o and lse must not overlap the inputs.
+ * Returns FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED or FA_ERR_HIP.
+ */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const float* q_descale, const float* k_descale, const float* v_descale,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                     void* stream);
+
+/*
  * fa_bwd_workspace_bytes - bytes of device workspace fa_bwd needs (one fp32
  * per query row, rounded up to 256). Returns 0 if the sizes are invalid.
  */

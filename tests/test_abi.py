@@ -18,7 +18,7 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_built_and_loads():
@@ -29,7 +29,8 @@ def test_library_built_and_loads():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_varlen_strided", "fa_bwd", "fa_bwd_workspace_bytes",
+    assert {"fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_varlen_strided", "fa_fwd_fp8", "fa_bwd",
+            "fa_bwd_workspace_bytes",
             "fa_decode", "fa_decode_paged", "fa_decode_workspace_bytes", "fa_status_string",
             "fa_last_error"} <= set(names)
     raw = ctypes.CDLL(fa.lib_path())
@@ -250,6 +251,33 @@ def test_bwd_workspace_bytes():
     assert fa.fa_bwd_workspace_bytes(1, 32, 8192) == 32 * 8192 * 4
     assert fa.fa_bwd_workspace_bytes(2, 3, 5) == 256
     assert fa.fa_bwd_workspace_bytes(0, 3, 5) == 0
+
+
+def fwd_fp8(**kw):
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, lse=None, qd=FAKE + 0x500000,
+             kd=FAKE + 0x500100, vd=FAKE + 0x500200, B=1, Hq=8, Hkv=2, Nq=128, Nk=128, d=128, scale=0.088, causal=1,
+             stream=None)
+    a.update(kw)
+    return fa.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["qd"], a["kd"], a["vd"], a["B"], a["Hq"],
+                         a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qd=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=FAKE + 0x100008), fa.FA_ERR_INVALID_ARG),       # misaligned
+    (dict(vd=FAKE + 0x500202), fa.FA_ERR_INVALID_ARG),      # misaligned descale
+    (dict(d=64), fa.FA_ERR_UNSUPPORTED),
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=1, Nq=200, Nk=128), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(o=FAKE + 0x1000), fa.FA_ERR_INVALID_ARG),         # o inside q
+    (dict(o=FAKE + 0x4fff00), fa.FA_ERR_INVALID_ARG),       # o over the q descales
+    (dict(lse=FAKE + 0x200010), fa.FA_ERR_INVALID_ARG),     # lse inside v
+])
+def test_fwd_fp8_rejects_before_launch(kw, status):
+    st = fwd_fp8(**kw)
+    assert st == status, (st, fa.fa_last_error())
 
 
 def dec_paged(**kw):

@@ -1,0 +1,91 @@
+"""FP8 (E4M3) prefill on the GPU (fa_fwd_fp8 through the C ABI) against the
+float64 oracle on the values the 8-bit inputs stand for (code * descale,
+exact in float64).
+
+Tolerance (the pages give none for FP8; derived from the arithmetic): the
+kernel rounds 2^8 P to E4M3 (3 mantissa bits, relative error up to 2^-4) for
+the second product; simulating exactly that rounding on the CPU over these
+workloads gives O rel-L2 of 1.9-2.4e-2 and max-abs up to 0.045 (on early
+causal rows, |O| up to 2.25). The bar is twice that: rel-L2 <= 5e-2, max-abs
+<= 0.1. The LSE is computed in fp32 from unrounded probabilities: <= 1e-3.
+Inputs: the seeded N(0,1) draws of the other workloads, quantized per
+(batch, head) slab with a power-of-two descale that maps max|x| to <= 448."""
+import math
+
+import numpy as np
+import pytest
+
+import attn_inputs as ai
+import oracle
+from gpu_util import announce
+
+pytestmark = pytest.mark.gpu
+
+O_REL_L2 = 5e-2
+O_MAX_ABS = 0.1
+LSE_MAX_ABS = 1e-3
+
+
+def to_dev_u8(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run(fa, x, causal):
+    import torch
+    q, k, v = (to_dev_u8(x[n]) for n in "qkv")
+    ds = [torch.from_numpy(x[n + "_descale"]).cuda() for n in "qkv"]
+    o, lse = fa.attention_fp8(q, k, v, *ds, causal=causal)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def check(o, lse, O_ref, L_ref, what):
+    import sys
+    assert np.all(np.isfinite(o)), f"{what}: non-finite O"
+    err = o - O_ref
+    rel = float(np.linalg.norm(err) / np.linalg.norm(O_ref))
+    mx = float(np.abs(err).max())
+    le = float(np.abs(lse - L_ref).max())
+    print(f"[parity] {what}: o_rel_l2={rel:.3e} o_max_abs={mx:.3e} lse_max_abs={le:.3e}", file=sys.stderr, flush=True)
+    assert rel <= O_REL_L2 and mx <= O_MAX_ABS and le <= LSE_MAX_ABS, (rel, mx, le)
+
+
+CASES = [
+    # B, Hq, Hkv, Nq, Nk, causal
+    (1, 4, 2, 256, 256, True),
+    (1, 8, 8, 300, 520, False),
+    (2, 4, 1, 200, 700, True),    # causal Nq < Nk (chunked prefill)
+    (1, 4, 4, 333, 333, True),    # ragged tiles
+    (1, 32, 8, 1024, 1024, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
+def test_fp8_vs_oracle(fa, case):
+    B, Hq, Hkv, Nq, Nk, causal = case
+    announce(f"fa_fwd_fp8 B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal}")
+    x = ai.prefill_inputs_fp8(700 + CASES.index(case), B, Hq, Hkv, Nq, 128, Nk=Nk)
+    o, lse = run(fa, x, causal)
+    f = {n: ai.fp8_to_f64(x[n], x[n + "_descale"]) for n in "qkv"}
+    O_ref, L_ref = oracle.attention(f["q"], f["k"], f["v"], 1.0 / math.sqrt(128), causal)
+    check(o, lse, O_ref, L_ref, f"fp8 {case}")
+
+
+def test_fp8_llama3_layer_sampled(fa):
+    """The Llama-3-8B GQA layer shape (B=1, Hq=32, Hkv=8, N=8192, causal) in
+    FP8: sampled rows of every head against the oracle over all keys."""
+    c = ai.CONFIGS["llama3_8b_gqa_n8192"]
+    Hq, Hkv, N = c["Hq"], c["Hkv"], c["N"]
+    announce("fa_fwd_fp8 Llama-3-8B layer N=8192")
+    x = ai.prefill_inputs_fp8(c["seed"], 1, Hq, Hkv, N, 128)
+    o, lse = run(fa, x, True)
+    f = {n: ai.fp8_to_f64(x[n], x[n + "_descale"]) for n in "qkv"}
+    rows = np.unique(np.r_[0, N - 1, np.random.default_rng(8).integers(0, N, 30)])
+    O_ref = np.empty((1, Hq, len(rows), 128))
+    L_ref = np.empty((1, Hq, len(rows)))
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        O_ref[0, h], L_ref[0, h] = oracle.attention_rows(f["q"][0, h, rows], rows, f["k"][0, g], f["v"][0, g],
+                                                         1.0 / math.sqrt(128), True, N)
+    check(o[:, :, rows], lse[:, :, rows], O_ref, L_ref, "fp8 llama3 sampled rows")

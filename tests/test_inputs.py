@@ -78,3 +78,33 @@ def test_decode_lengths_in_range():
     cfg = ai.CONFIGS["decode_32seq_gqa"]
     lens = ai.decode_lengths(cfg["seed"], cfg["B"], cfg["len_lo"], cfg["len_hi"])
     assert lens.min() >= 1024 and lens.max() <= 32768 and len(lens) == 32
+
+
+def test_fp8_e4m3_codec():
+    """OCP E4M3: known codes, every finite code round-trips, ties go to the
+    even code, the largest finite value is 448 and NaN is 0x7F / 0xFF."""
+    import math
+    d = ai.fp8_decode(np.arange(256, dtype=np.uint8))
+    assert d[0x38] == 1.0 and d[0xB8] == -1.0 and d[0x7E] == 448.0
+    assert d[0x08] == 2.0 ** -6 and d[0x01] == 2.0 ** -9 and d[0x07] == 7 * 2.0 ** -9
+    assert d[0x39] == 1.125 and d[0x40] == 2.0 and d[0x00] == 0.0
+    assert math.isnan(d[0x7F]) and math.isnan(d[0xFF]) and np.sum(np.isnan(d)) == 2
+    codes = np.arange(256, dtype=np.uint8)
+    fin = ~np.isnan(d) & (codes != 0x80)
+    assert np.array_equal(ai.fp8_encode(d[fin]), codes[fin])
+    # midpoints: 1.0625 between 0x38 and 0x39 -> 0x38 (even); 1.1875 -> 0x3A
+    assert ai.fp8_encode(np.array([1.0625, 1.1875, -1.0625]))[:3].tolist() == [0x38, 0x3A, 0xB8]
+    assert ai.fp8_encode(np.array([1000.0]))[0] == 0x7E
+
+
+def test_fp8_quantize_is_exact_scaling():
+    x = np.random.default_rng(3).standard_normal((64, 128)).astype(np.float32)
+    codes, ds = ai.fp8_quantize(x)
+    assert ds == 2.0 ** np.ceil(np.log2(np.abs(x).max() / 448.0))
+    back = ai.fp8_decode(codes) * ds
+    assert np.abs(back).max() <= 448 * ds
+    # relative rounding error of normal values within half an E4M3 ulp (2^-4)
+    big = np.abs(x) > 2.0 ** -6 * ds * 2
+    assert np.max(np.abs(back[big] - x[big]) / np.abs(x[big])) <= 2.0 ** -4
+    y = ai.prefill_inputs_fp8(5, 1, 2, 1, 16, 128)
+    assert y["q"].dtype == np.uint8 and y["q_descale"].shape == (1, 2) and y["k_descale"].shape == (1, 1)
