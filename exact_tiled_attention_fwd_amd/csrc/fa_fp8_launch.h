@@ -25,7 +25,7 @@ struct Fp8Args {
   int causal;
 };
 
-constexpr int kFp8BlockRows = 128;  // query rows per FP8 workgroup
+constexpr int kFp8BlockRows = 256;  // query rows per FP8 workgroup
 
 hipError_t launch_fwd_fp8(const Fp8Args& a, hipStream_t stream);
 

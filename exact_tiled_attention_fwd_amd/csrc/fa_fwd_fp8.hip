@@ -10,15 +10,18 @@
 // score scale folds the q and k descales in; the v descale is applied once in
 // the epilogue.
 //
-// Structure: one workgroup of 4 waves owns 128 query rows of one (b, q-head)
-// (32 rows per wave) and walks 64-key tiles of its kv-head, double-buffered in
-// LDS through registers (one barrier per tile):
+// Structure: one workgroup of 8 waves owns 256 query rows of one (b, q-head)
+// (32 rows per wave) and walks 64-key tiles of its kv-head. As in the 16-bit
+// kernels, two groups of 4 waves alternate on the same SIMDs, one issuing
+// matrix-core work while the other runs its softmax; group 0 stages V and
+// group 1 stages K through registers into 2-slot LDS rings:
 //   S^T = K Q^T             A = K rows from LDS, B = Q^T held in registers
-//   online softmax          the tile's row maximum is taken every tile, and
-//                           P is formed as exp2(s c - m + 8): every value lies
-//                           in (0, 256], inside E4M3's range, and small ones
-//                           keep normal precision; the 2^8 cancels against the
-//                           running sum, which accumulates the same values
+//   online softmax          p = 2^(s c - m + 4) against the running
+//                           reference m; the row maximum is taken only on a
+//                           row's first tile or when some lane's sum exceeds
+//                           448 (E4M3's largest value, which then bounds
+//                           every p); the 2^4 keeps small values normal and
+//                           cancels against the running sum
 //   O^T += V^T P^T          A = V^T from LDS, B = P rounded to E4M3 (RNE)
 // V is transposed on its way into LDS (4x4 byte blocks, v_perm_b32), with the
 // keys of each row stored in the order a lane holds its 32 P values, so every
@@ -32,7 +35,7 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kThreads = 256;                 // 4 waves
+constexpr int kThreads = 512;                 // 8 waves = 2 groups of 4
 constexpr int kBM = kFp8BlockRows;            // 128 query rows
 constexpr int kD = 128;                       // head width (bytes per row in fp8)
 constexpr int kRows = 64;                     // keys per tile
@@ -41,7 +44,8 @@ constexpr int kVtStride = kRows + 16;         // V^T tile row: 64 keys + 16 byte
 constexpr int kKBytes = kRows * kKStride;     // 8 KiB
 constexpr int kVtBytes = kD * kVtStride;      // 10 KiB
 constexpr int kStage = kKBytes + kVtBytes;
-constexpr float kPOffset = 8.f;               // P is scaled by 2^8 before rounding
+constexpr float kPOffset = 4.f;               // P is scaled by 2^4 before rounding
+constexpr float kSumLimit8 = 448.f;           // largest finite E4M3 value
 
 __device__ inline f32x16 mfma_f8(const i32x8& a, const i32x8& b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -88,57 +92,122 @@ __device__ inline void transpose4(uint32_t a, uint32_t b, uint32_t c, uint32_t d
   out[3] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
 }
 
-// Global -> register staging of one tile (rows at or beyond nvalid re-read
-// row nvalid - 1; their scores are masked). K: two 16-byte chunks per thread.
-// V: two 4-key x 4-byte blocks per thread (a wave covers 128 contiguous bytes
-// of 2 x 4 key rows per load).
-struct TileRegs8 {
-  u32x4 k[2];
-  uint32_t v[2][4];
-};
-
-__device__ inline void load_tile8(const uint8_t* __restrict__ kb, const uint8_t* __restrict__ vb, int nvalid,
-                                  TileRegs8& t) {
+// Global -> register staging of one tile by the 256 threads of one group
+// (t = thread index in the group). Rows at or beyond nvalid re-read row
+// nvalid - 1; their scores are masked. K: two 16-byte chunks per thread.
+// V: two blocks of 4 keys x 4 bytes per thread (for each key row a wave
+// covers 128 contiguous bytes of 2 rows per load).
+__device__ inline void load_k8(const uint8_t* __restrict__ kb, int nvalid, int t, u32x4 (&r)[2]) {
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const int idx = threadIdx.x + kThreads * p;
+    const int idx = t + 256 * p;
     const int row = min(idx >> 3, nvalid - 1), c = idx & 7;
-    t.k[p] = *reinterpret_cast<const u32x4*>(kb + (size_t)row * kD + 16 * c);
+    r[p] = *reinterpret_cast<const u32x4*>(kb + (size_t)row * kD + 16 * c);
+  }
+}
+__device__ inline void store_k8(char* __restrict__ kl, int t, const u32x4 (&r)[2]) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int idx = t + 256 * p;
+    const int row = idx >> 3, c = idx & 7;
+    *reinterpret_cast<u32x4*>(kl + row * kKStride + kpos(row, c) * 16) = r[p];
+  }
+}
+__device__ inline void load_v8(const uint8_t* __restrict__ vb, int nvalid, int t, uint32_t (&r)[2][4]) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int idx = t + 256 * p;
     const int dq = idx & 31, kq = idx >> 5;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int vr = min(4 * kq + i, nvalid - 1);
-      t.v[p][i] = *reinterpret_cast<const uint32_t*>(vb + (size_t)vr * kD + 4 * dq);
+      r[p][i] = *reinterpret_cast<const uint32_t*>(vb + (size_t)vr * kD + 4 * dq);
     }
   }
 }
-
-__device__ inline void store_tile8(char* __restrict__ st, const TileRegs8& t) {
-  char* kl = st;
-  char* vl = st + kKBytes;
+__device__ inline void store_v8(char* __restrict__ vl, int t, const uint32_t (&r)[2][4]) {
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const int idx = threadIdx.x + kThreads * p;
-    const int row = idx >> 3, c = idx & 7;
-    *reinterpret_cast<u32x4*>(kl + row * kKStride + kpos(row, c) * 16) = t.k[p];
+    const int idx = t + 256 * p;
     const int dq = idx & 31, kq = idx >> 5;
     uint32_t cols[4];
-    transpose4(t.v[p][0], t.v[p][1], t.v[p][2], t.v[p][3], cols);
+    transpose4(r[p][0], r[p][1], r[p][2], r[p][3], cols);
     const int pos = vt_pos(4 * kq);
 #pragma unroll
     for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(vl + (4 * dq + j) * kVtStride + pos) = cols[j];
   }
 }
 
+// Exponentials of one tile against reference m (log2 units): p = 2^(s c -
+// m + kPOffset), packed four per register as E4M3 in the order of vt_pos.
+// Returns this lane's sum of the unrounded values.
+__device__ __attribute__((always_inline)) inline float exp_pack8(const f32x16 (&s)[2], float c, float m,
+                                                                  uint32_t (&pk)[8]) {
+  const float sub = m - kPOffset;
+  float psum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * mm + i], c, -sub));
+        psum += p[i];
+      }
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      pk[4 * kb + mm] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
+    }
+  return psum;
+}
+
+// Online softmax step of one tile. The tile is first exponentiated against
+// the current reference m_run; every value is at most its lane's sum, so if
+// every lane's sum is at most kSumLimit the values fit E4M3 and are kept.
+// Otherwise (or on a row's first tile) the tile's row maximum is taken, m_run
+// moves to it, the running sum and accumulator are rescaled, and the tile is
+// exponentiated again (then every value is at most 2^kPOffset).
+__device__ __attribute__((always_inline)) inline void softmax8(const f32x16 (&s)[2], float c, float& m_run,
+                                                                float& l_run, f32x16 (&acc_o)[4], uint32_t (&pk)[8]) {
+  float psum = 0.f;
+  bool slow = __builtin_amdgcn_ballot_w64(m_run == -__builtin_inff()) != 0;
+  if (!slow) {
+    psum = exp_pack8(s, c, m_run, pk);
+    slow = __builtin_amdgcn_ballot_w64(!(psum <= kSumLimit8)) != 0;
+  }
+  if (slow) {
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    const float m_new = fmaxf(m_run, halves_max(mx) * c);
+    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    l_run *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
+    m_run = m_new;
+    psum = exp_pack8(s, c, m_use, pk);
+  }
+  l_run += psum;
+}
+
 template <bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8_kernel(
+__global__ __launch_bounds__(kThreads, 1) void fa_fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, const float* __restrict__ q_ds,
     const float* __restrict__ k_ds, const float* __restrict__ v_ds, int B, int Hq, int Hkv, int Nq, int Nk,
     float scale_log2, int n_qt) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStage];
+  __shared__ __attribute__((aligned(16))) char smem[2 * kKBytes + 2 * kVtBytes];
+  char* const kring = smem;                // K tile t in slot t & 1
+  char* const vring = smem + 2 * kKBytes;  // V^T tile t in slot t & 1
   const Work wk = map_work(blockIdx.x, B, Hq, Hkv, n_qt);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
+  const int grp = wave >> 2;           // 0: matrix cores first, stages V; 1: softmax first, stages K
+  const int gtid = threadIdx.x & 255;  // thread index within the group
   const int q0 = wk.qt * kBM;
   const int q0w = q0 + 32 * wave;
   const int qrow = q0w + (lane & 31);
@@ -151,10 +220,17 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8_kernel(
   const float c = scale_log2 * q_ds[bh] * k_ds[bg];
   const float vd = v_ds[bg];
 
+  // key tiles this workgroup visits, and those this wave computes on
   int n_kv = (Nk + kRows - 1) / kRows;
   if (CAUSAL) {
     const int last_key = min(q0 + kBM, Nq) - 1 + off;
     n_kv = last_key < 0 ? 0 : min(n_kv, last_key / kRows + 1);
+  }
+  const bool wave_active = q0w < Nq;
+  int wt = wave_active ? n_kv : 0;
+  if (CAUSAL && wave_active) {
+    const int last = min(q0w + 31, Nq - 1) + off;
+    wt = last < 0 ? 0 : min(n_kv, last / kRows + 1);
   }
 
   // Q^T operand: row qrow, head-dim bytes 64 ks + 32 h .. +31.
@@ -171,32 +247,12 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8_kernel(
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[mt][r] = 0.f;
-  float m_run = -__builtin_inff();  // running row maximum, log2 units
-  float l_run = 0.f;                // this lane's share of the running sum of 2^8 P
+  float m_run = -__builtin_inff();  // running reference, log2 units
+  float l_run = 0.f;                // this lane's share of the running sum
+  f32x16 s[2];                      // S^T of the tile last multiplied
+  uint32_t pk[8];                   // P of the tile last softmaxed (E4M3)
 
-  TileRegs8 tr;
-  if (n_kv > 0) {
-    load_tile8(kp, vp, min(kRows, Nk), tr);
-    store_tile8(smem, tr);
-  }
-  __syncthreads();
-  for (int j = 0; j < n_kv; ++j) {
-    if (j + 1 < n_kv)
-      load_tile8(kp + (size_t)(j + 1) * kRows * kD, vp + (size_t)(j + 1) * kRows * kD, min(kRows, Nk - (j + 1) * kRows),
-                 tr);
-    const char* kl = smem + (j & 1) * kStage;
-    const char* vl = kl + kKBytes;
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma_f8(k_op(kl, kb, ks, lane), qop[ks], s[kb]);
-
-    // mask the ragged tail and the causal diagonal
+  auto softmax = [&](int j) {
     const int j0 = j * kRows;
     const bool need_mask = (j0 + kRows > Nk) || (CAUSAL && j0 + kRows - 1 > q0w + off);
     if (need_mask) {
@@ -207,48 +263,68 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp8_kernel(
         for (int r = 0; r < 16; ++r)
           if (j0 + 32 * kb + acc_key(r, half) >= lim) s[kb][r] = -__builtin_inff();
     }
-    // online softmax with the tile's row maximum
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = halves_max(mx) * c;
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-    if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      l_run *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
-    }
-    m_run = m_new;
-    const float sub = m_use - kPOffset;
-    uint32_t pk[8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        float p[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * mm + i], c, -sub));
-          l_run += p[i];
-        }
-        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-        pk[4 * kb + mm] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], lo, true);
-      }
+    softmax8(s, c, m_run, l_run, acc_o, pk);
+  };
+  // matrix-core phase: O^T += V^T_jo P^T (do_o) and S^T = K_js Q^T (do_s), interleaved
+  auto mma = [&](bool do_o, int jo, bool do_s, int js) {
+    const char* vl = vring + (jo & 1) * kVtBytes;
+    const char* kl = kring + (js & 1) * kKBytes;
     const i32x8 bp = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
+    if (do_s) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc_o[mt] = mfma_f8(vt_op(vl, mt, lane), bp, acc_o[mt]);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (do_o) acc_o[t] = mfma_f8(vt_op(vl, t, lane), bp, acc_o[t]);
+      if (do_s) s[t & 1] = mfma_f8(k_op(kl, t & 1, t >> 1, lane), qop[t >> 1], s[t & 1]);
+    }
+  };
+  auto tile_rows = [&](int j) { return min(kRows, Nk - j * kRows); };
 
-    if (j + 1 < n_kv) store_tile8(smem + ((j + 1) & 1) * kStage, tr);
+  // Each group runs its own loop (both pass the same barriers):
+  //   group 0: A = store V_i, load V_{i+1}, O(i-1), S(i)   B = softmax(i)
+  //   group 1: A = load K_{i+1}, softmax(i-1)              B = O(i-1), S(i), store K_{i+1}
+  // V_i / K_i live in ring slot i & 1; a slot is rewritten only after the
+  // barrier that ends the last phase reading its previous tile.
+  if (grp == 0) {
+    uint32_t rv[2][4];
+    if (n_kv > 0) {
+      load_v8(vp, tile_rows(0), gtid, rv);
+      store_v8(vring, gtid, rv);
+      if (n_kv > 1) load_v8(vp + (size_t)kRows * kD, tile_rows(1), gtid, rv);
+    }
     __syncthreads();
+    for (int i = 0; i <= n_kv; ++i) {
+      if (i >= 1 && i < n_kv) {
+        store_v8(vring + (i & 1) * kVtBytes, gtid, rv);
+        if (i + 1 < n_kv) load_v8(vp + (size_t)(i + 1) * kRows * kD, tile_rows(i + 1), gtid, rv);
+      }
+      mma(i >= 1 && i - 1 < wt, i - 1, i < wt, i);
+      __syncthreads();
+      if (i < wt) softmax(i);
+      __syncthreads();
+    }
+  } else {
+    u32x4 rk[2];
+    if (n_kv > 0) {
+      load_k8(kp, tile_rows(0), gtid, rk);
+      store_k8(kring, gtid, rk);
+    }
+    __syncthreads();
+    for (int i = 0; i <= n_kv; ++i) {
+      if (i + 1 < n_kv) load_k8(kp + (size_t)(i + 1) * kRows * kD, tile_rows(i + 1), gtid, rk);
+      if (i >= 1 && i - 1 < wt) softmax(i - 1);
+      __syncthreads();
+      mma(i >= 1 && i - 1 < wt, i - 1, i < wt, i);
+      if (i + 1 < n_kv) store_k8(kring + ((i + 1) & 1) * kKBytes, gtid, rk);
+      __syncthreads();
+    }
   }
 
-  if (qrow >= Nq) return;
+  if (!wave_active || qrow >= Nq) return;
   const float l_tot = halves_sum(l_run);
   const float inv = l_tot > 0.f ? vd / l_tot : 0.f;
   uint16_t* orow = o + (bh * Nq + qrow) * kD;
