@@ -106,6 +106,30 @@ struct Stage {
   }
 };
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One 1 KiB direct-to-LDS load: lane l's 16 bytes from sbase + voff land at
+// LDS address lds + 16 l. Written as asm so that the compiler's wait
+// insertion does not wait for these loads before every LDS read; the tile
+// loop waits for them itself before its barrier.
+__device__ __attribute__((always_inline)) inline void dma16(const uint16_t* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// Source byte offset, in a [64][D] tile, of the chunk that load instruction
+// i of wave w writes to LDS chunk position p = 256 i + 64 w + lane (row
+// p / (D/8), position p % (D/8)); the XOR swizzle of chunk_pos is an
+// involution, so position -> chunk uses the same map. Rows at or beyond
+// nvalid re-read row nvalid - 1.
+template <int D>
+__device__ inline uint32_t dma_off(int i, int w, int lane, int nvalid) {
+  constexpr int CPR = D / 8;
+  const int p = 256 * i + 64 * w + lane;
+  const int row = p / CPR, pos = p % CPR;
+  return (uint32_t)(min(row, nvalid - 1) * (D * 2) + chunk_pos<D>(row, pos) * 16);
+}
+
 // LSE in log2 units, +inf where the row does not exist or saw no key, so
 // that exp2(s c - lse2) is 0 there.
 __device__ inline float lse2_of(const float* __restrict__ lse, int row, int n) {
@@ -305,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(
 
 // ------------------------------------------------------------------ dQ
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fa_bwd_dq_kernel(
+__global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dq, int B, int Hq, int Hkv, int Nq, int Nk, float scale, float c2, int n_qt) {
@@ -348,22 +372,26 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dq_kernel(
     n_kv = last_key < 0 ? 0 : min(n_kv, last_key / kTileRows + 1);
   }
 
-  u32x4 rk[ST::NP], rv[ST::NP];
-  auto fetch = [&](int j) {
-    ST::load(k + kvo + (size_t)j * kTileRows * D, Nk - j * kTileRows, rk);
-    ST::load(v + kvo + (size_t)j * kTileRows * D, Nk - j * kTileRows, rv);
+  // K_j and V_j go HBM -> LDS directly (slot j & 1), issued one tile ahead;
+  // each wave's loads are waited for (vmcnt) before the barrier that ends
+  // the tile, so the next tile is complete for every wave after it.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)smem;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform for the scalar LDS address
+  auto issue = [&](int j) {
+    const int nvalid = min(kTileRows, Nk - j * kTileRows);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint16_t* base = (t ? v : k) + kvo + (size_t)j * kTileRows * D;
+      const uint32_t slot = lds0 + (uint32_t)((j & 1) * 2 * TILE + t * TILE + 64 * wv * 16);
+#pragma unroll
+      for (int i = 0; i < TILE / 4096; ++i) dma16(base, dma_off<D>(i, wv, lane, nvalid), slot + 4096 * i);
+    }
   };
-  auto put = [&](int slot) {
-    ST::store(smem + slot * 2 * TILE, rk);
-    ST::store(smem + slot * 2 * TILE + TILE, rv);
-  };
-  if (n_kv > 0) {
-    fetch(0);
-    put(0);
-  }
+  if (n_kv > 0) issue(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q, dO operands and tile 0
   __syncthreads();
   for (int j = 0; j < n_kv; ++j) {
-    if (j + 1 < n_kv) fetch(j + 1);
+    if (j + 1 < n_kv) issue(j + 1);
     const char* kt = smem + (j & 1) * 2 * TILE;
     const char* vt = kt + TILE;
     // S^T = K Q^T and dP^T = V dO^T for both 32-key blocks (four chains)
@@ -408,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dq_kernel(
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32<DT>(tr_op<D>(kt, G, mt, lane), bs, acc[mt]);
     }
-    if (j + 1 < n_kv) put((j + 1) & 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile j + 1 has landed
     __syncthreads();
   }
 
