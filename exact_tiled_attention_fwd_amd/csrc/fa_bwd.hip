@@ -174,8 +174,22 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_delta_kernel(const uint16_t* 
 }
 
 // ------------------------------------------------------------------ dK, dV
+// 8 waves: wave w owns keys 32 (w % 4) .. +31 of the workgroup's 128 and rows
+// 32 (w / 4) .. +31 of every 64-row query tile, so two waves (one per half
+// of the rows) accumulate partial dK, dV for the same keys; the halves are
+// added through LDS at the end.
+constexpr int kDkdvThreads = 512;
+
+template <int D>
+__device__ inline uint32_t dma_off8(int i, int w, int lane, int nvalid) {  // 8 loading waves
+  constexpr int CPR = D / 8;
+  const int p = 512 * i + 64 * w + lane;
+  const int row = p / CPR, pos = p % CPR;
+  return (uint32_t)(min(row, nvalid - 1) * (D * 2) + chunk_pos<D>(row, pos) * 16);
+}
+
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(
+__global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
@@ -183,25 +197,41 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(
   constexpr int KS = D / 16, MT = D / 32;
   constexpr int TILE = kTileRows * D * 2;
   constexpr int BUF = 2 * TILE + 2 * kTileRows * 4;  // Q, dO, lse2, delta
-  using ST = Stage<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF];
+  constexpr int KL_BYTES = kBwdKeyRows * D * 2;      // K rows of the workgroup's keys
+  constexpr int RED = MT * 16 * 256 * 4;             // one accumulator set of 4 waves
+  constexpr int SMEM = 2 * BUF + KL_BYTES > RED ? 2 * BUF + KL_BYTES : RED;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  char* const kls = smem + 2 * BUF;
 
   const int nbg = B * Hkv;
   const int kt = blockIdx.x / nbg, bg = blockIdx.x % nbg;  // key tiles from the first: heaviest first
   const int b = bg / Hkv, g = bg % Hkv, grp = Hq / Hkv;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform for the scalar LDS address
+  const int kw = wave & 3, rh = wave >> 2;               // key group, row half of each tile
   const int kt0 = kt * kBwdKeyRows;
-  const int key = kt0 + 32 * wave + (lane & 31);  // this lane's key column
-  const int off = Nk - Nq;                        // causal: key j visible to query i iff j <= i + off
+  const int wk0 = kt0 + 32 * kw;                         // first key of this wave
+  const int key = wk0 + (lane & 31);                     // this lane's key column
+  const int off = Nk - Nq;                               // causal: key j visible to query i iff j <= i + off
 
-  // K and V rows of this wave's 32 keys: B operands of S = Q K^T, dP = dO V^T.
+  // V rows of this wave's 32 keys in registers (B operand of dP = dO V^T);
+  // the K rows of all 128 keys in LDS (B operand of S = Q K^T, read per use).
   const size_t kvo = (size_t)bg * Nk * D;
   const int krow = min(key, Nk - 1);
-  u32x4 kop[KS], vop[KS];
+  u32x4 vop[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    kop[ks] = *reinterpret_cast<const u32x4*>(k + kvo + (size_t)krow * D + 16 * ks + 8 * half);
+  for (int ks = 0; ks < KS; ++ks)
     vop[ks] = *reinterpret_cast<const u32x4*>(v + kvo + (size_t)krow * D + 16 * ks + 8 * half);
+  {
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int p = 0; p < kBwdKeyRows * CPR / kDkdvThreads; ++p) {
+      const int idx = threadIdx.x + kDkdvThreads * p;
+      const int row = idx / CPR, c = idx % CPR;
+      const int src = min(kt0 + row, Nk - 1);
+      *reinterpret_cast<u32x4*>(kls + row * (D * 2) + chunk_pos<D>(row, c) * 16) =
+          *reinterpret_cast<const u32x4*>(k + kvo + (size_t)src * D + c * 8);
+    }
   }
   f32x16 acc_dk[MT], acc_dv[MT];
 #pragma unroll
@@ -217,100 +247,125 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(
   const int per_head = max(0, n_t - t_first);
   const int total = grp * per_head;
 
-  u32x4 rq[ST::NP], rdo[ST::NP];
-  float rl = 0.f;  // lse2 (threads 0..63) or delta (threads 64..127) of one row
-  auto fetch = [&](int it) {
+  // Q and dO tiles go HBM -> LDS directly (slot it & 1), one tile ahead; the
+  // tile's LSE (log2 units) and delta go through one register of threads
+  // 0..127. Each wave waits for its own loads before the tile barrier.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)smem;
+  float rl = 0.f;
+  auto issue = [&](int it) {
     const int h = g * grp + it / per_head, t = t_first + it % per_head;
     const size_t qo = ((size_t)b * Hq + h) * Nq;
     const int i0 = t * kTileRows;
-    ST::load(q + (qo + i0) * D, Nq - i0, rq);
-    ST::load(dout + (qo + i0) * D, Nq - i0, rdo);
+    const int nvalid = min(kTileRows, Nq - i0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint16_t* base = (u ? dout : q) + (qo + i0) * D;
+      const uint32_t slot = lds0 + (uint32_t)((it & 1) * BUF + u * TILE + 64 * wv * 16);
+#pragma unroll
+      for (int i = 0; i < TILE / 8192; ++i) dma16(base, dma_off8<D>(i, wv, lane, nvalid), slot + 8192 * i);
+    }
     if (threadIdx.x < kTileRows)
       rl = lse2_of(lse + qo + i0, threadIdx.x, Nq - i0);
     else if (threadIdx.x < 2 * kTileRows)
       rl = (i0 + (int)threadIdx.x - kTileRows < Nq) ? delta[qo + i0 + threadIdx.x - kTileRows] : 0.f;
   };
-  auto put = [&](int slot) {
-    char* base = smem + slot * BUF;
-    ST::store(base, rq);
-    ST::store(base + TILE, rdo);
-    if (threadIdx.x < 2 * kTileRows) reinterpret_cast<float*>(base + 2 * TILE)[threadIdx.x] = rl;
+  auto put_rl = [&](int it) {
+    if (threadIdx.x < 2 * kTileRows) reinterpret_cast<float*>(smem + (it & 1) * BUF + 2 * TILE)[threadIdx.x] = rl;
   };
 
   if (total > 0) {
-    fetch(0);
-    put(0);
+    issue(0);
+    put_rl(0);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   for (int it = 0; it < total; ++it) {
-    if (it + 1 < total) fetch(it + 1);
+    if (it + 1 < total) issue(it + 1);
     const char* qt = smem + (it & 1) * BUF;
     const char* dot = qt + TILE;
     const float* l2 = reinterpret_cast<const float*>(qt + 2 * TILE);
     const float* dl = l2 + kTileRows;
     const int i0 = (t_first + it % per_head) * kTileRows;
-    // S = Q K^T and dP = dO V^T for both 32-row blocks (four independent chains)
-    f32x16 s[2], dp[2];
+    const int r0 = i0 + 32 * rh;  // first query row of this wave in the tile
+    // skip a block entirely above the causal diagonal
+    if (!CAUSAL || wk0 <= r0 + 31 + off) {
+      f32x16 s, dp;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[qb][r] = dp[qb][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = mfma32<DT>(row_op<D>(qt, 32 * qb + (lane & 31), 2 * ks + half), kop[ks], s[qb]);
-        dp[qb] = mfma32<DT>(row_op<D>(dot, 32 * qb + (lane & 31), 2 * ks + half), vop[ks], dp[qb]);
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma32<DT>(row_op<D>(qt, 32 * rh + (lane & 31), 2 * ks + half),
+                       row_op<D>(kls, 32 * kw + (lane & 31), 2 * ks + half), s);
+        dp = mfma32<DT>(row_op<D>(dot, 32 * rh + (lane & 31), 2 * ks + half), vop[ks], dp);
       }
-    // Masking is needed only where this wave's keys reach past the tile's
-    // first row (causal diagonal) or past Nk (ragged key tile).
-    const int wk0 = kt0 + 32 * wave;
-    const bool need_mask = (wk0 + 31 >= Nk) || (CAUSAL && wk0 + 31 > i0 + off);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // P and dS; register r holds query row 32 qb + acc_key(r, half).
+      // masking only where this wave's keys reach past its first row or Nk
+      const bool need_mask = (wk0 + 31 >= Nk) || (CAUSAL && wk0 + 31 > r0 + off);
+      // P and dS; register r holds query row 32 rh + acc_key(r, half) of the tile.
       uint32_t pk[8], dsk[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int rl0 = 32 * qb + 8 * m + 4 * half;
+        const int rl0 = 32 * rh + 8 * m + 4 * half;
         const f32x4 L = *reinterpret_cast<const f32x4*>(l2 + rl0);
         const f32x4 Dv = *reinterpret_cast<const f32x4*>(dl + rl0);
         float p[4], ds[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * m + e;
-          float x = exp2_fast(__builtin_fmaf(s[qb][r], c2, -L[e]));
+          float x = exp2_fast(__builtin_fmaf(s[r], c2, -L[e]));
           if (need_mask) {
             const bool hide = (key >= Nk) | (CAUSAL & (key > i0 + rl0 + e + off));
             x = hide ? 0.f : x;
           }
           p[e] = x;
-          ds[e] = x * (dp[qb][r] - Dv[e]);
+          ds[e] = x * (dp[r] - Dv[e]);
         }
         pk[2 * m] = pack2<DT>(p[0], p[1]);
         pk[2 * m + 1] = pack2<DT>(p[2], p[3]);
         dsk[2 * m] = pack2<DT>(ds[0], ds[1]);
         dsk[2 * m + 1] = pack2<DT>(ds[2], ds[3]);
       }
-      // dV^T += dO^T P, dK^T += Q^T dS (the next block's exponentials can
-      // overlap these)
+      // dV^T += dO^T P, dK^T += Q^T dS over this wave's 32 rows
 #pragma unroll
       for (int G = 0; G < 2; ++G) {
         const u32x4 bp = {pk[4 * G], pk[4 * G + 1], pk[4 * G + 2], pk[4 * G + 3]};
         const u32x4 bs = {dsk[4 * G], dsk[4 * G + 1], dsk[4 * G + 2], dsk[4 * G + 3]};
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          acc_dv[mt] = mfma32<DT>(tr_op<D>(dot, 2 * qb + G, mt, lane), bp, acc_dv[mt]);
-          acc_dk[mt] = mfma32<DT>(tr_op<D>(qt, 2 * qb + G, mt, lane), bs, acc_dk[mt]);
+          acc_dv[mt] = mfma32<DT>(tr_op<D>(dot, 2 * rh + G, mt, lane), bp, acc_dv[mt]);
+          acc_dk[mt] = mfma32<DT>(tr_op<D>(qt, 2 * rh + G, mt, lane), bs, acc_dk[mt]);
         }
       }
     }
-    if (it + 1 < total) put((it + 1) & 1);
+    if (it + 1 < total) put_rl(it + 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile it + 1 has landed
     __syncthreads();
   }
 
-  if (key >= Nk) return;
+  // Add the two row halves' partial sums (through LDS, register-major so a
+  // register of all 256 lanes of a half is one contiguous row), then write.
   // acc register r of block mt holds d = 32 mt + acc_key(r, half) of this key.
+  float* red = reinterpret_cast<float*>(smem);
+  const int rlane = kw * 64 + lane;
+  auto reduce = [&](f32x16 (&acc)[MT]) {
+    if (rh == 1) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[(mt * 16 + r) * 256 + rlane] = acc[mt][r];
+    }
+    __syncthreads();
+    if (rh == 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mt][r] += red[(mt * 16 + r) * 256 + rlane];
+    }
+    __syncthreads();
+  };
+  reduce(acc_dk);
+  reduce(acc_dv);
+
+  if (rh != 0 || key >= Nk) return;
   uint16_t* dkr = dk + kvo + (size_t)key * D;
   uint16_t* dvr = dv + kvo + (size_t)key * D;
 #pragma unroll
@@ -320,10 +375,10 @@ __global__ __launch_bounds__(kThreads, 1) void fa_bwd_dkdv_kernel(
       const int d0 = 32 * mt + 8 * m + 4 * half;
       const u32x2 wk = {pack2<DT>(acc_dk[mt][4 * m] * scale, acc_dk[mt][4 * m + 1] * scale),
                         pack2<DT>(acc_dk[mt][4 * m + 2] * scale, acc_dk[mt][4 * m + 3] * scale)};
-      const u32x2 wv = {pack2<DT>(acc_dv[mt][4 * m], acc_dv[mt][4 * m + 1]),
-                        pack2<DT>(acc_dv[mt][4 * m + 2], acc_dv[mt][4 * m + 3])};
+      const u32x2 wvv = {pack2<DT>(acc_dv[mt][4 * m], acc_dv[mt][4 * m + 1]),
+                         pack2<DT>(acc_dv[mt][4 * m + 2], acc_dv[mt][4 * m + 3])};
       *reinterpret_cast<u32x2*>(dkr + d0) = wk;
-      *reinterpret_cast<u32x2*>(dvr + d0) = wv;
+      *reinterpret_cast<u32x2*>(dvr + d0) = wvv;
     }
 }
 
@@ -465,7 +520,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t stream) {
   const float c2 = a.scale * kLog2e;
   hipLaunchKernelGGL((fa_bwd_delta_kernel<DT, D>), dim3((unsigned)nb_delta), dim3(kThreads), 0, stream,
                      (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)nb_kv), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)nb_kv), dim3(kDkdvThreads), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse,
                      a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale, c2);
   hipLaunchKernelGGL((fa_bwd_dq_kernel<DT, D, CAUSAL>), dim3((unsigned)nb_q), dim3(kThreads), 0, stream,
