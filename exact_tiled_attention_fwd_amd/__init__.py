@@ -16,7 +16,8 @@ Tensor-level helpers:
                      causal=False, scale=None) -> (o, lse)
         q [Hq,total_q,d], k/v [Hkv,total_k,d], any strides likewise
     flash_attn_func(q, k, v, dropout_p=0.0, softmax_scale=None, causal=False)
-        -> o, for q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d]
+        -> o, for q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d]; differentiable (fa_bwd)
+        when an input requires grad
     flash_attn_varlen_func(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
                            max_seqlen_k, dropout_p=0.0, softmax_scale=None,
                            causal=False) -> o, for q [total_q,Hq,d]
@@ -340,15 +341,46 @@ def _no_dropout(dropout_p):
         raise FAUnsupported(FA_ERR_UNSUPPORTED, "dropout is not supported (forward inference path only)")
 
 
+class _AttentionFn(torch.autograd.Function):
+    """Autograd node over fa_fwd / fa_bwd for [B,H,N,d] tensors (any strides
+    in the forward; the backward reads contiguous copies)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal, scale):
+        o, lse = attention(q, k, v, causal=causal, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal, ctx.scale = causal, scale
+        ctx.mark_non_differentiable(lse)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, _dlse):
+        q, k, v, o, lse = ctx.saved_tensors
+        qc, kc, vc, oc, doc = (t.contiguous() for t in (q, k, v, o, do))
+        dq, dk, dv = attention_bwd(qc, kc, vc, oc, lse, doc, causal=ctx.causal, scale=ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def _needs_grad(*ts):
+    return torch.is_grad_enabled() and any(t.requires_grad for t in ts)
+
+
 def flash_attn_func(q, k, v, dropout_p: float = 0.0, softmax_scale: float | None = None, causal: bool = False,
                     return_lse: bool = False):
     """The flash_attn_func calling convention: q [B,Nq,Hq,d], k/v [B,Nk,Hkv,d]
     (batch, seq, heads, dim); returns o [B,Nq,Hq,d] in the same layout (and
     the LSE [B,Hq,Nq] fp32 with return_lse). No copies: the kernels read and
-    write the (batch, seq, heads, dim) tensors through their strides."""
+    write the (batch, seq, heads, dim) tensors through their strides. When
+    an input requires grad, the result is differentiable: the backward pass
+    runs fa_bwd (on contiguous copies)."""
     _no_dropout(dropout_p)
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(name, t, 4, strided=True)
+    if _needs_grad(q, k, v):
+        scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(q.shape[-1])
+        o, lse = _AttentionFn.apply(q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2), bool(causal), scale)
+        out = o.transpose(1, 2)
+        return (out, lse) if return_lse else out
     out = torch.empty_like(q)
     o, lse = attention(q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2), causal=causal,
                        scale=softmax_scale, out=out.transpose(1, 2))

@@ -116,3 +116,24 @@ def test_bwd_llama3_layer_sampled(fa):
         got = (from_dev(dq[:, hs.start:hs.stop], dt), from_dev(dk[:, g:g + 1], dt), from_dev(dv[:, g:g + 1], dt))
         check_grads([got[0][:, :, rows], got[1][:, :, rows], got[2][:, :, rows]],
                     [ref[0][:, :, rows], ref[1][:, :, rows], ref[2][:, :, rows]], f"bwd llama3 kv-head {g}")
+
+
+def test_flash_attn_func_autograd(fa):
+    """flash_attn_func on tensors that require grad: loss.backward() runs
+    fa_bwd, and the gradients match the float64 oracle (BSHD layout, GQA,
+    causal)."""
+    import torch
+    B, Hq, Hkv, N, d, dt = 1, 8, 2, 300, 128, ai.BF16
+    announce("flash_attn_func autograd")
+    x = ai.prefill_inputs(640, B, Hq, Hkv, N, d, dt)
+    do_bits = ai.grad_output(640, B, Hq, N, d, dt)
+    q, k, v = (to_dev(x[n], dt).transpose(1, 2).contiguous().requires_grad_(True) for n in "qkv")
+    do = to_dev(do_bits, dt).transpose(1, 2).contiguous()
+    out = fa.flash_attn_func(q, k, v, causal=True)
+    assert out.requires_grad and tuple(out.shape) == (B, N, Hq, d)
+    out.backward(do)
+    torch.cuda.synchronize()
+    f = lambda a: ai.bits_to_f64(a, dt)
+    ref = oracle.attention_bwd(f(x["q"]), f(x["k"]), f(x["v"]), f(do_bits), 1.0 / math.sqrt(d), True)
+    got = [from_dev(t.grad.transpose(1, 2), dt) for t in (q, k, v)]
+    check_grads(got, ref, "flash_attn_func autograd")
