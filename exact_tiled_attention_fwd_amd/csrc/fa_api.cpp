@@ -97,11 +97,14 @@ fa::DecodePlan make_plan(int B, int Hkv, int Lcap, int num_splits, int Hq, int d
   fa::DecodePlan p;
   p.chunk = (int)chunk;
   p.n_split = (int)(((long long)Lcap + chunk - 1) / chunk);
-  const size_t rows = (size_t)B * Hq * p.n_split;
+  p.slots = p.n_split + 1;
+  const size_t rows = (size_t)B * Hq * p.slots;
   const size_t o_bytes = ((rows * d * sizeof(float)) + 255) & ~(size_t)255;
   const size_t l_bytes = ((rows * sizeof(float)) + 255) & ~(size_t)255;
+  const size_t h_bytes = (((size_t)B + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
   p.ws_lse_offset = o_bytes;
-  p.ws_bytes = o_bytes + l_bytes;
+  p.ws_hdr_offset = o_bytes + l_bytes;
+  p.ws_bytes = o_bytes + l_bytes + h_bytes;
   return p;
 }
 
@@ -309,8 +312,8 @@ fa_status decode_impl(const char* fn, const void* q, const void* k_cache, const 
     return fail(FA_ERR_INVALID_ARG, "o or workspace overlaps another tensor");
   st = check_device();
   if (st != FA_OK) return st;
-  fa::DecodeArgs a{q, k_cache, v_cache, seqlens, o, lse, workspace, p.ws_lse_offset, B, Hq, Hkv, Lcap, d, scale,
-                   p.chunk, p.n_split, dtype, table, page_size, max_pages, num_pages};
+  fa::DecodeArgs a{q, k_cache, v_cache, seqlens, o, lse, workspace, p.ws_lse_offset, p.ws_hdr_offset, B, Hq, Hkv,
+                   Lcap, d, scale, p.chunk, p.slots, dtype, table, page_size, max_pages, num_pages};
   hipError_t e = fa::launch_decode(a, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(FA_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(e));
   return FA_OK;

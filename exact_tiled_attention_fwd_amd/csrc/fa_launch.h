@@ -35,10 +35,15 @@ struct FwdArgs {
 };
 
 // Decode key split: chunk keys per workgroup, n_split chunks cover Lcap rows.
+// Decode split plan. The split kernel gives every wave an equal share of the
+// cached rows (at least `chunk` of them), so one (sequence, kv-head) pair
+// yields at most n_split + 1 partial results ("slots").
 struct DecodePlan {
   int chunk;
   int n_split;
+  int slots;             // partial results per (sequence, q-head): n_split + 1
   size_t ws_lse_offset;  // bytes from workspace start to the LSE partials
+  size_t ws_hdr_offset;  // bytes from workspace start to the split header
   size_t ws_bytes;       // total workspace bytes
 };
 
@@ -50,10 +55,10 @@ struct DecodeArgs {
   void* o;
   float* lse;
   void* workspace;
-  size_t ws_lse_offset;
+  size_t ws_lse_offset, ws_hdr_offset;
   int B, Hq, Hkv, Lcap, d;
   float scale;
-  int chunk, n_split;
+  int chunk, slots;
   int dtype;
   // Paged cache (block_table != nullptr): k_cache / v_cache are
   // [num_pages, Hkv, page_size, d] and Lcap = max_pages * page_size.

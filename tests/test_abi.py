@@ -307,14 +307,18 @@ def test_decode_paged_rejects_before_launch(kw, status):
 
 
 def test_decode_workspace_bytes():
+    # Layout: O partials [B, Hq, slots, d] fp32, LSE partials [B, Hq, slots]
+    # fp32, split header (B + 1) int32, each rounded up to 256 bytes; slots =
+    # splits + 1 (a wave's equal share of the rows may start inside a chunk).
+    r256 = lambda x: (x + 255) // 256 * 256
     # auto plan for the 32-sequence, 32K-cache shape: 512-key chunks, 64 splits
     n = fa.fa_decode_workspace_bytes(32, 32, 8, 32768, 128, 0)
-    rows = 32 * 32 * 64
-    assert n == rows * 128 * 4 + rows * 4
+    rows = 32 * 32 * 65
+    assert n == r256(rows * 128 * 4) + r256(rows * 4) + r256(33 * 4)
     # explicit splits: chunk rounded up to a multiple of 128 keys
     n1 = fa.fa_decode_workspace_bytes(1, 4, 1, 1000, 64, 3)   # chunk 334 -> 384, 3 splits
-    assert n1 == (4 * 3 * 64 * 4 + 255) // 256 * 256 + 256
-    assert fa.fa_decode_workspace_bytes(1, 4, 1, 1000, 64, 1) == 4 * 64 * 4 + 256
+    assert n1 == r256(4 * 4 * 64 * 4) + r256(4 * 4 * 4) + r256(2 * 4)
+    assert fa.fa_decode_workspace_bytes(1, 4, 1, 1000, 64, 1) == r256(4 * 2 * 64 * 4) + 256 + 256
     assert fa.fa_decode_workspace_bytes(0, 4, 1, 1000, 64, 0) == 0
     assert fa.fa_decode_workspace_bytes(1, 4, 1, 1000, 96, 0) == 0
     assert fa.fa_decode_workspace_bytes(1, 4, 1, 1000, 64, -1) == 0
