@@ -87,8 +87,9 @@ fa::DecodePlan make_plan(int B, int Hkv, int Lcap, int num_splits, int Hq, int d
   if (num_splits > 0) {
     chunk = ((long long)Lcap + num_splits - 1) / num_splits;
   } else {
-    // Enough workgroups to cover the GPU several times over, chunks of at
-    // least one tile; long caches get 512-key chunks.
+    // The smallest share of rows a split wave takes: 512 keys for long
+    // caches, less (down to one 128-row tile) when there are few rows in
+    // all, so that small batches still spread over many waves.
     chunk = 512;
     while (chunk > R && (long long)B * Hkv * (((long long)Lcap + chunk - 1) / chunk) < 4096) chunk /= 2;
   }

@@ -239,8 +239,10 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
 /*
  * fa_decode_workspace_bytes - bytes of device workspace fa_decode needs for
  * these sizes and this `num_splits` (0 = the library's choice). Returns 0 if
- * the sizes are invalid. The workspace holds per-split partial outputs and
- * their LSE (the merge identity in LSE form).
+ * the sizes are invalid. The workspace holds the partial outputs and their
+ * LSE (the merge identity in LSE form), at most splits + 1 of them per
+ * (sequence, q-head) with splits = num_splits or the library's choice, and a
+ * small header that the split pass leaves for the merge pass.
  */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Lcap, int d, int num_splits);
 
@@ -268,8 +270,10 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Lcap, int d, int nu
  *            the caller; contents on entry are ignored.
  *   d        64 or 128; Hq / Hkv must be <= 32
  *   scale    finite and > 0
- *   num_splits  number of key chunks per sequence for a cache of Lcap rows,
- *            0 = chosen by the library; the result does not depend on it
+ *   num_splits  sets the smallest share of cached rows one wave takes,
+ *            ceil(Lcap / num_splits) rounded up to a multiple of 128 (shares
+ *            are otherwise equal across the waves the GPU holds at once);
+ *            0 = chosen by the library. The result does not depend on it
  *            beyond rounding.
  *
  * Returns FA_OK, FA_ERR_INVALID_ARG (including a too-small workspace),
