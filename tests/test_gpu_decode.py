@@ -104,3 +104,30 @@ def test_decode_deterministic(fa):
     o2, l2 = fa.decode(q, kc, vc, sl)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_many_sequences(fa):
+    # More than 64 sequences (the split walks the sequences 64 at a time),
+    # short caches (a wave's share spans several (sequence, kv-head) pairs
+    # and pairs are cut between waves), every 7th sequence empty.
+    import torch
+    lens = np.random.default_rng(25).integers(0, 301, 150).astype(np.int32)
+    lens[::7] = 0
+    announce(f"decode many sequences B=150 lens={list(lens[:8])}")
+    x = ai.decode_inputs(25, 150, 8, 2, 300, 64, ai.BF16, lens)
+    q, kc, vc, sl = dev_inputs(x)
+    o, lse = fa.decode(q, kc, vc, sl)
+    torch.cuda.synchronize()
+    o_np, l_np = from_dev(o, ai.BF16), lse.cpu().numpy()
+    empty = lens == 0
+    assert np.all(o_np[empty] == 0) and np.all(np.isneginf(l_np[empty]))
+    xs = {k: (v[~empty] if k in ("q", "k_cache", "v_cache", "seqlens") else v) for k, v in x.items()}
+    O_ref, L_ref = oracle_decode(xs, 1.0 / math.sqrt(64))
+    compare(o_np[~empty], O_ref, l_np[~empty], L_ref, "decode B150")
+
+
+def test_most_partials_per_pair(fa):
+    # Sequence 0 (6 blocks of 32) shifts sequence 1 (32 blocks) into the
+    # middle of the first wave's share; with 384-row shares sequence 1 then
+    # gets ceil(1000 / 384) + 1 = 4 partials, the most the workspace holds.
+    decode_case(fa, 26, 2, 4, 1, 1000, 64, ai.BF16, [192, 1000], num_splits=3)

@@ -38,6 +38,8 @@ SMALL = [
     (4, 32, 8, 2048, 128, ai.BF16, [0, 129, 2047, 640], 128),
     (2, 4, 4, 512, 64, ai.FP16, [511, 64], 64),
     (2, 16, 2, 4096, 128, ai.FP16, [4096, 3333], 256),
+    # more than 64 sequences, short caches: shares span several pairs
+    (70, 8, 2, 256, 128, ai.BF16, [int(v) for v in np.random.default_rng(31).integers(0, 257, 70)], 32),
 ]
 
 
