@@ -134,9 +134,9 @@ struct BlockWalk {
   }
 };
 
-// One wave per workgroup. The d = 128 kernel is asked to keep its register
-// use down so that several chunks stay in flight per SIMD; the d = 64 kernel
-// needs no such hint (forcing it makes the compiler spill).
+// One wave per workgroup. At d = 128 a wave holds about 340 registers (Q,
+// the O accumulator and one block of K and V in flight), so one wave runs
+// per SIMD; capping it at 256 for two waves per SIMD measured slower.
 //
 // Wave w of W takes stream blocks [w S, (w + 1) S), S = max(ceil(T / W),
 // chunk / 32) for a stream of T blocks. Its partial of pair (b, g) goes to
@@ -144,7 +144,7 @@ struct BlockWalk {
 // most ceil(Lcap / chunk) + 1 slots. Wave 0 also writes S and every pre_b to
 // the header (hdr[0] = S, hdr[1 + b] = pre_b) for the combine kernel.
 template <int DT, int D, bool PAGED>
-__global__ __launch_bounds__(64, D == 128 ? 8 : 1) void fa_decode_split_kernel(
+__global__ __launch_bounds__(64) void fa_decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ seqlens, float* __restrict__ ws_o, float* __restrict__ ws_lse,
     int32_t* __restrict__ hdr, int B, int Hq, int Hkv, int Lcap, int chunk, int slots, float scale_log2,
