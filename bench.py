@@ -113,6 +113,16 @@ def counter_traffic(name):
     return float(m_b.group(1))
 
 
+def counter_clock_ghz(name):
+    """Shader clock (GHz) measured during the kernel, from a committed counter
+    summary whose kernel sources still hash to the recorded value; else None."""
+    path = os.path.join(PROFILES, name)
+    if counter_traffic(name) is None:
+        return None
+    m = re.search(r"dispatch time:\s*([0-9.]+) GHz", open(path).read())
+    return float(m.group(1)) if m else None
+
+
 # ------------------------------------------------------------------ device data
 def to_dev(bits, dtype):
     import torch
@@ -526,6 +536,7 @@ def main():
                             "llama3_8b_gqa_n8192_fp8") else pname
         peak = MFMA_PEAK_FP8_TFLOPS if cfg.endswith("_fp8") else MFMA_PEAK_TFLOPS
         out["prefill"] = {"workload": f"{wl} causal={causal}", "ms_mean": round(t_ms, 4),
+                          "ms_median": round(float(np.median(per[i])), 4),
                           "ms_min": round(float(np.min(per[i])), 4), "tflops": round(tflops, 2),
                           "frac_mfma_peak": round(tflops / peak, 4)}
         prof = cfg if cfg in ("llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd", "llama3_8b_gqa_n8192_fp8") else pname
@@ -534,6 +545,12 @@ def main():
         out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                            "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic,
                            "algorithmic_bytes": pre.bytes, "flops_per_launch": pre.flops}
+        # The published peak assumes 2.4 GHz; the committed profile records the
+        # clock the kernel actually ran at, and the fraction of the peak at it.
+        ghz = counter_clock_ghz(f"fa_{kind}_{prof}_counters.md") if causal else None
+        if ghz:
+            out["roofline"]["clock_ghz"] = ghz
+            out["roofline"]["frac_at_clock"] = round(tflops / (peak * ghz / 2.4), 4)
         i += 1
     if dec is not None:
         t_ms = float(np.mean(per[i]))
@@ -541,7 +558,8 @@ def main():
         droof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                  "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic(f"fa_{cfg if paged else 'decode_32seq_gqa'}_counters.md"),
                  "algorithmic_bytes": dec.bytes}
-        out["decode"] = {"workload": cfg if paged else "decode_32seq_gqa", "ms_mean": round(t_ms, 4), "ms_min": round(float(np.min(per[i])), 4),
+        out["decode"] = {"workload": cfg if paged else "decode_32seq_gqa", "ms_mean": round(t_ms, 4),
+                         "ms_median": round(float(np.median(per[i])), 4), "ms_min": round(float(np.min(per[i])), 4),
                          "value": round(gbs, 1), "unit": "GB/s", "roofline": droof}
         if pre is None:
             out.update(value=round(gbs, 1), unit="GB/s", roofline=droof)
