@@ -26,6 +26,8 @@
 // V is transposed on its way into LDS (4x4 byte blocks, v_perm_b32), with the
 // keys of each row stored in the order a lane holds its 32 P values, so every
 // operand is two 16-byte LDS reads and no lane exchanges are needed.
+#include <type_traits>
+
 #include "fa_fp8_launch.h"
 #include "fa_tile.h"
 
@@ -36,7 +38,7 @@ namespace {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 512;                 // 8 waves = 2 groups of 4
-constexpr int kBM = kFp8BlockRows;            // 128 query rows
+constexpr int kBM = kFp8BlockRows;            // 256 query rows
 constexpr int kD = 128;                       // head width (bytes per row in fp8)
 constexpr int kRows = 64;                     // keys per tile
 constexpr int kKStride = kD;                  // K tile row: 128 bytes
@@ -265,12 +267,21 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_fp8_kernel(
     }
     softmax8(s, c, m_run, l_run, acc_o, pk);
   };
-  // matrix-core phase: O^T += V^T_jo P^T (do_o) and S^T = K_js Q^T (do_s), interleaved
-  auto mma = [&](bool do_o, int jo, bool do_s, int js) {
+  // Matrix-core phase: O^T += V^T_jo P^T (DO_O) and S^T = K_js Q^T (DO_S),
+  // interleaved. All A operands of the phase are read from LDS first, so the
+  // MFMAs wait for the reads once instead of each in turn.
+  auto mma_t = [&](auto do_o_t, auto do_s_t, int jo, int js) {
+    constexpr bool DO_O = decltype(do_o_t)::value, DO_S = decltype(do_s_t)::value;
     const char* vl = vring + (jo & 1) * kVtBytes;
     const char* kl = kring + (js & 1) * kKBytes;
+    i32x8 ao[4], as[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if constexpr (DO_O) ao[t] = vt_op(vl, t, lane);
+      if constexpr (DO_S) as[t] = k_op(kl, t & 1, t >> 1, lane);
+    }
     const i32x8 bp = {(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
-    if (do_s) {
+    if constexpr (DO_S) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -278,9 +289,17 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_fp8_kernel(
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      if (do_o) acc_o[t] = mfma_f8(vt_op(vl, t, lane), bp, acc_o[t]);
-      if (do_s) s[t & 1] = mfma_f8(k_op(kl, t & 1, t >> 1, lane), qop[t >> 1], s[t & 1]);
+      if constexpr (DO_O) acc_o[t] = mfma_f8(ao[t], bp, acc_o[t]);
+      if constexpr (DO_S) s[t & 1] = mfma_f8(as[t], qop[t >> 1], s[t & 1]);
     }
+  };
+  auto mma = [&](bool do_o, int jo, bool do_s, int js) {
+    if (do_o && do_s)
+      mma_t(std::true_type{}, std::true_type{}, jo, js);
+    else if (do_o)
+      mma_t(std::true_type{}, std::false_type{}, jo, js);
+    else if (do_s)
+      mma_t(std::false_type{}, std::true_type{}, jo, js);
   };
   auto tile_rows = [&](int j) { return min(kRows, Nk - j * kRows); };
 
