@@ -12,9 +12,11 @@
 //
 // Structure: one workgroup of 8 waves owns 256 query rows of one (b, q-head)
 // (32 rows per wave) and walks 64-key tiles of its kv-head. As in the 16-bit
-// kernels, two groups of 4 waves alternate on the same SIMDs, one issuing
-// matrix-core work while the other runs its softmax; group 0 stages V and
-// group 1 stages K through registers into 2-slot LDS rings:
+// head-width-128 kernel, two groups of 4 waves alternate on the same SIMDs,
+// one issuing matrix-core work while the other runs its softmax, and the
+// waves of group 0 move every K and V tile HBM -> LDS directly
+// (global_load_lds_dwordx4) into 4-slot rings, K two tiles and V one tile
+// ahead, with one barrier per step:
 //   S^T = K Q^T             A = K rows from LDS, B = Q^T held in registers
 //   online softmax          p = 2^(s c - m + 4) against the running
 //                           reference m; the row maximum is taken only on a
@@ -22,10 +24,10 @@
 //                           448 (E4M3's largest value, which then bounds
 //                           every p); the 2^4 keeps small values normal and
 //                           cancels against the running sum
-//   O^T += V^T P^T          A = V^T from LDS, B = P rounded to E4M3 (RNE)
-// V is transposed on its way into LDS (4x4 byte blocks, v_perm_b32), with the
-// keys of each row stored in the order a lane holds its 32 P values, so every
-// operand is two 16-byte LDS reads and no lane exchanges are needed.
+//   O^T += V^T P^T          A = V^T gathered from the row-major V tile with
+//                           transposed 8-bit LDS reads (ds_read_b64_tr_b8),
+//                           in the key order of the P operand; B = P rounded
+//                           to E4M3 (RNE)
 #include <type_traits>
 
 #include "fa_fp8_launch.h"
@@ -36,18 +38,18 @@ namespace fa {
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kThreads = 512;                 // 8 waves = 2 groups of 4
-constexpr int kBM = kFp8BlockRows;            // 256 query rows
-constexpr int kD = 128;                       // head width (bytes per row in fp8)
-constexpr int kRows = 64;                     // keys per tile
-constexpr int kKStride = kD;                  // K tile row: 128 bytes
-constexpr int kVtStride = kRows + 16;         // V^T tile row: 64 keys + 16 bytes of padding
-constexpr int kKBytes = kRows * kKStride;     // 8 KiB
-constexpr int kVtBytes = kD * kVtStride;      // 10 KiB
-constexpr int kStage = kKBytes + kVtBytes;
-constexpr float kPOffset = 4.f;               // P is scaled by 2^4 before rounding
-constexpr float kSumLimit8 = 448.f;           // largest finite E4M3 value
+constexpr int kThreads = 512;           // 8 waves = 2 groups of 4
+constexpr int kBM = kFp8BlockRows;      // 256 query rows
+constexpr int kD = 128;                 // head width = bytes per row in fp8
+constexpr int kRows = 64;               // keys per tile
+constexpr int kSlots = 4;               // ring depth for K and for V
+constexpr int kTile = kRows * kD;       // 8 KiB
+constexpr float kPOffset = 4.f;         // P is scaled by 2^4 before rounding
+constexpr float kSumLimit8 = 448.f;     // largest finite E4M3 value
 
 __device__ inline f32x16 mfma_f8(const i32x8& a, const i32x8& b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
@@ -57,87 +59,82 @@ __device__ inline i32x8 cat(const u32x4& lo, const u32x4& hi) {
   return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-// K tile: row r, 16-byte chunk c (0..7) stored at chunk position c ^ (r & 7).
-__device__ inline int kpos(int r, int c) { return c ^ (r & 7); }
+// LDS tiles are row-major [64 keys][128 bytes], 8 chunks of 16 bytes a row.
+//   K: chunk c of row r at position c ^ ((r / 2) % 8). An A-operand read
+//      takes one chunk column of 32 rows; each 16 rows of it fill all banks.
+//   V: chunk c of row r at position c ^ 2 ((r / 2) % 2 + 2 ((r / 8) % 2)).
+//      A transposed read takes 8 key rows x 2 chunks per 16 lanes (32 bytes
+//      a row, two 8-byte halves); the 16 rows of a half-wave (keys k and
+//      k + 4) then fill all banks.
+// Both maps are involutions in c, so position -> chunk is the same map.
+__device__ inline int k_phys(int r, int c) { return c ^ ((r >> 1) & 7); }
+__device__ inline int v_phys(int r, int c) { return c ^ (2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1))); }
 
-// Position of key k (0..63) in a V^T row. A lane in half h holds, in its P
-// accumulator registers r of key block kb, keys 32 kb + 8 (r/4) + 4 h + r%4;
-// packed in register order those are bytes 16 kb + r of the lane's operand,
-// and V^T stores key k at 32 h + that byte index.
-__device__ inline int vt_pos(int k) {
-  return 32 * ((k >> 2) & 1) + 16 * (k >> 5) + 4 * ((k >> 3) & 3) + (k & 3);
+// Byte offset in the global tile of the 16-byte chunk that load instruction
+// i (0, 1) of wave w (0..3 of group 0) writes to LDS position
+// p = 256 i + 64 w + lane (row p / 8, position p % 8). Rows at or beyond
+// nvalid re-read row nvalid - 1; their scores are masked to -inf. The
+// swizzles depend on the row only through row % 16, so for a full tile the
+// offset of instruction 1 is that of instruction 0 plus 32 rows.
+template <bool IS_V>
+__device__ inline uint32_t dma_src(int i, int w, int lane, int nvalid) {
+  const int p = 256 * i + 64 * w + lane;
+  const int row = p >> 3, pos = p & 7;
+  const int c = IS_V ? v_phys(row, pos) : k_phys(row, pos);
+  return (uint32_t)(min(row, nvalid - 1) * kD + c * 16);
 }
 
-// A operand of S^T = K Q^T: key 32 kb + lane % 32, head-dim bytes 64 ks + 32 h .. +31.
+// One 1 KiB direct-to-LDS load: lane l's 16 bytes from sbase + voff land at
+// LDS address lds + 16 l. Asm, so that the compiler's wait insertion, which
+// cannot tell ring slots apart, does not wait for every load in flight before
+// each LDS read; the step barriers do the waiting.
+__device__ __attribute__((always_inline)) inline void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// Barrier after waiting until this thread has at most `pending` (0, 2 or 4,
+// wave-uniform) direct-to-LDS loads outstanding.
+__device__ __attribute__((always_inline)) inline void dma_barrier(int pending) {
+  if (pending >= 4)
+    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+  else if (pending >= 2)
+    __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2)
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// A operand of S^T = K Q^T: key 32 kb + lane % 32, head-dim bytes
+// 64 ks + 32 h .. +31 (chunks 4 ks + 2 h and the next).
 __device__ inline i32x8 k_op(const char* __restrict__ kl, int kb, int ks, int lane) {
   const int r = 32 * kb + (lane & 31), c = 4 * ks + 2 * (lane >> 5);
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(kl + r * kKStride + kpos(r, c) * 16);
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(kl + r * kKStride + kpos(r, c + 1) * 16);
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(kl + r * kD + k_phys(r, c) * 16);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(kl + r * kD + k_phys(r, c + 1) * 16);
   return cat(lo, hi);
 }
 
-// A operand of O^T += V^T P^T: head-dim row 32 mt + lane % 32, key bytes 32 h .. +31.
+// A operand of O^T += V^T P^T for head-dim rows 32 mt ..: byte b of lane l
+// is V[key(b)][32 mt + l % 32] with key(b) = 32 (b / 16) + 8 ((b % 16) / 4)
+// + 4 h + b % 4 (h = l / 32), the key order in which a lane packs its P
+// values. ds_read_b64_tr_b8 gives lane i of each 16-lane group byte i % 8 of
+// the 8 bytes addressed by lane 2 e + i / 8, as its byte e (e = 0..7); so in
+// read t lane 2 e + s of a group addresses key row key(8 t + e), head-dim
+// bytes 32 mt + 16 g + 8 s (g = (l / 16) % 2), and every lane ends up with
+// bytes 8 t .. 8 t + 7 of its operand.
 __device__ inline i32x8 vt_op(const char* __restrict__ vl, int mt, int lane) {
-  const char* p = vl + (32 * mt + (lane & 31)) * kVtStride + 32 * (lane >> 5);
-  return cat(*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 16));
-}
-
-// 4x4 byte transpose: rows a, b, c, d (4 bytes each) -> columns.
-__device__ inline void transpose4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t (&out)[4]) {
-  const uint32_t ab_lo = __builtin_amdgcn_perm(b, a, 0x05010400u);  // a0 b0 a1 b1
-  const uint32_t ab_hi = __builtin_amdgcn_perm(b, a, 0x07030602u);  // a2 b2 a3 b3
-  const uint32_t cd_lo = __builtin_amdgcn_perm(d, c, 0x05010400u);  // c0 d0 c1 d1
-  const uint32_t cd_hi = __builtin_amdgcn_perm(d, c, 0x07030602u);  // c2 d2 c3 d3
-  out[0] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);        // a0 b0 c0 d0
-  out[1] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);        // a1 b1 c1 d1
-  out[2] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);
-  out[3] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
-}
-
-// Global -> register staging of one tile by the 256 threads of one group
-// (t = thread index in the group). Rows at or beyond nvalid re-read row
-// nvalid - 1; their scores are masked. K: two 16-byte chunks per thread.
-// V: two blocks of 4 keys x 4 bytes per thread (for each key row a wave
-// covers 128 contiguous bytes of 2 rows per load).
-__device__ inline void load_k8(const uint8_t* __restrict__ kb, int nvalid, int t, u32x4 (&r)[2]) {
+  const int j = lane & 15, e = j >> 1, s = j & 1, g = (lane >> 4) & 1, h = lane >> 5;
+  const int c = 2 * mt + g;
+  i32x8 out;
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int idx = t + 256 * p;
-    const int row = min(idx >> 3, nvalid - 1), c = idx & 7;
-    r[p] = *reinterpret_cast<const u32x4*>(kb + (size_t)row * kD + 16 * c);
+  for (int t = 0; t < 4; ++t) {
+    const int key = 32 * (t >> 1) + 16 * (t & 1) + 8 * (e >> 2) + 4 * h + (e & 3);
+    const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (lds_i32x2_t*)(vl + key * kD + v_phys(key, c) * 16 + 8 * s));
+    out[2 * t] = w[0];
+    out[2 * t + 1] = w[1];
   }
-}
-__device__ inline void store_k8(char* __restrict__ kl, int t, const u32x4 (&r)[2]) {
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int idx = t + 256 * p;
-    const int row = idx >> 3, c = idx & 7;
-    *reinterpret_cast<u32x4*>(kl + row * kKStride + kpos(row, c) * 16) = r[p];
-  }
-}
-__device__ inline void load_v8(const uint8_t* __restrict__ vb, int nvalid, int t, uint32_t (&r)[2][4]) {
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int idx = t + 256 * p;
-    const int dq = idx & 31, kq = idx >> 5;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int vr = min(4 * kq + i, nvalid - 1);
-      r[p][i] = *reinterpret_cast<const uint32_t*>(vb + (size_t)vr * kD + 4 * dq);
-    }
-  }
-}
-__device__ inline void store_v8(char* __restrict__ vl, int t, const uint32_t (&r)[2][4]) {
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int idx = t + 256 * p;
-    const int dq = idx & 31, kq = idx >> 5;
-    uint32_t cols[4];
-    transpose4(r[p][0], r[p][1], r[p][2], r[p][3], cols);
-    const int pos = vt_pos(4 * kq);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(vl + (4 * dq + j) * kVtStride + pos) = cols[j];
-  }
+  return out;
 }
 
 // Exponentials of one tile against reference m (log2 units): p = 2^(s c -
@@ -197,19 +194,42 @@ __device__ __attribute__((always_inline)) inline void softmax8(const f32x16 (&s)
   l_run += psum;
 }
 
+// The 4 tile loads of one step (K_{i+2}: 2, V_{i+1}: 2 instructions per
+// wave), slotted in after MFMAs 1, 3, 5, 7 of a full 8-op matrix-core phase.
+// Full tiles only.
+struct DmaSpread {
+  const uint8_t* kbase;
+  const uint8_t* vbase;
+  uint32_t kslot, vslot;
+  bool has_k, has_v;
+  uint32_t dk, dv;
+  __device__ __attribute__((always_inline)) void operator()(int t) const {
+    if ((t & 1) == 0) return;
+    const int j = t >> 1;
+    if (j < 2) {
+      if (has_k) dma16(kbase + 32 * kD * j, dk, kslot + 4096 * j);
+    } else {
+      if (has_v) dma16(vbase + 32 * kD * (j - 2), dv, vslot + 4096 * (j - 2));
+    }
+  }
+};
+struct NoDma {
+  __device__ void operator()(int) const {}
+};
+
 template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, const float* __restrict__ q_ds,
     const float* __restrict__ k_ds, const float* __restrict__ v_ds, int B, int Hq, int Hkv, int Nq, int Nk,
     float scale_log2, int n_qt) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kKBytes + 2 * kVtBytes];
-  char* const kring = smem;                // K tile t in slot t & 1
-  char* const vring = smem + 2 * kKBytes;  // V^T tile t in slot t & 1
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kSlots * kTile];
+  char* const kring = smem;                   // K tile t in slot t % 4
+  char* const vring = smem + kSlots * kTile;  // V tile t in slot t % 4
   const Work wk = map_work(blockIdx.x, B, Hq, Hkv, n_qt);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
-  const int grp = wave >> 2;           // 0: matrix cores first, stages V; 1: softmax first, stages K
-  const int gtid = threadIdx.x & 255;  // thread index within the group
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int grp = wave >> 2;  // 0: matrix cores first, issues the tile loads; 1: softmax first
   const int q0 = wk.qt * kBM;
   const int q0w = q0 + 32 * wave;
   const int qrow = q0w + (lane & 31);
@@ -243,6 +263,10 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_fp8_kernel(
     const uint8_t* p = qp + (size_t)qr * kD + 64 * ks + 32 * half;
     qop[ks] = cat(*reinterpret_cast<const u32x4*>(p), *reinterpret_cast<const u32x4*>(p + 16));
   }
+  // Wait for Q (and the descales) here, once: the tile loads are asm the
+  // compiler does not count, so a wait it placed inside the loop would also
+  // wait for them.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   f32x16 acc_o[4];
 #pragma unroll
@@ -268,12 +292,12 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_fp8_kernel(
     softmax8(s, c, m_run, l_run, acc_o, pk);
   };
   // Matrix-core phase: O^T += V^T_jo P^T (DO_O) and S^T = K_js Q^T (DO_S),
-  // interleaved. All A operands of the phase are read from LDS first, so the
-  // MFMAs wait for the reads once instead of each in turn.
-  auto mma_t = [&](auto do_o_t, auto do_s_t, int jo, int js) {
+  // interleaved. All A operands of the phase are read from LDS first; ex(n)
+  // runs after the n-th MFMA.
+  auto mma_t = [&](auto do_o_t, auto do_s_t, int jo, int js, const auto& ex) {
     constexpr bool DO_O = decltype(do_o_t)::value, DO_S = decltype(do_s_t)::value;
-    const char* vl = vring + (jo & 1) * kVtBytes;
-    const char* kl = kring + (js & 1) * kKBytes;
+    const char* vl = vring + (jo % kSlots) * kTile;
+    const char* kl = kring + (js % kSlots) * kTile;
     i32x8 ao[4], as[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -287,59 +311,103 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_fp8_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
     }
+    int n = 0;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      if constexpr (DO_O) acc_o[t] = mfma_f8(ao[t], bp, acc_o[t]);
-      if constexpr (DO_S) s[t & 1] = mfma_f8(as[t], qop[t >> 1], s[t & 1]);
+      if constexpr (DO_O) {
+        acc_o[t] = mfma_f8(ao[t], bp, acc_o[t]);
+        ex(n++);
+      }
+      if constexpr (DO_S) {
+        s[t & 1] = mfma_f8(as[t], qop[t >> 1], s[t & 1]);
+        ex(n++);
+      }
     }
   };
   auto mma = [&](bool do_o, int jo, bool do_s, int js) {
     if (do_o && do_s)
-      mma_t(std::true_type{}, std::true_type{}, jo, js);
+      mma_t(std::true_type{}, std::true_type{}, jo, js, NoDma{});
     else if (do_o)
-      mma_t(std::true_type{}, std::false_type{}, jo, js);
+      mma_t(std::true_type{}, std::false_type{}, jo, js, NoDma{});
     else if (do_s)
-      mma_t(std::false_type{}, std::true_type{}, jo, js);
+      mma_t(std::false_type{}, std::true_type{}, jo, js, NoDma{});
   };
-  auto tile_rows = [&](int j) { return min(kRows, Nk - j * kRows); };
 
-  // Each group runs its own loop (both pass the same barriers):
-  //   group 0: A = store V_i, load V_{i+1}, O(i-1), S(i)   B = softmax(i)
-  //   group 1: A = load K_{i+1}, softmax(i-1)              B = O(i-1), S(i), store K_{i+1}
-  // V_i / K_i live in ring slot i & 1; a slot is rewritten only after the
-  // barrier that ends the last phase reading its previous tile.
-  if (grp == 0) {
-    uint32_t rv[2][4];
-    if (n_kv > 0) {
-      load_v8(vp, tile_rows(0), gtid, rv);
-      store_v8(vring, gtid, rv);
-      if (n_kv > 1) load_v8(vp + (size_t)kRows * kD, tile_rows(1), gtid, rv);
+  // ---- direct-to-LDS tile loads, issued by the waves of group 0 only (they
+  // wait at the step barrier anyway): 2 instructions per wave per tile.
+  const uint32_t lds_k = (uint32_t)(uintptr_t)(lds_void_t*)kring;
+  const uint32_t lds_v = (uint32_t)(uintptr_t)(lds_void_t*)vring;
+  const int wg = wv & 3;  // wave index within its group
+  const uint32_t dk = dma_src<false>(0, wg, lane, kRows);  // source offsets of a full tile
+  const uint32_t dv = dma_src<true>(0, wg, lane, kRows);
+  auto issue = [&](bool is_v, int t) {
+    const int nvalid = min(kRows, Nk - t * kRows);
+    const uint8_t* base = (is_v ? vp : kp) + (size_t)t * kRows * kD;
+    const uint32_t slot = (is_v ? lds_v : lds_k) + (uint32_t)((t % kSlots) * kTile) + (uint32_t)(64 * wg * 16);
+    if (nvalid == kRows) {
+      dma16(base, is_v ? dv : dk, slot);
+      dma16(base + 32 * kD, is_v ? dv : dk, slot + 4096);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        dma16(base, is_v ? dma_src<true>(i, wg, lane, nvalid) : dma_src<false>(i, wg, lane, nvalid), slot + 4096 * i);
     }
-    __syncthreads();
-    for (int i = 0; i <= n_kv; ++i) {
-      if (i >= 1 && i < n_kv) {
-        store_v8(vring + (i & 1) * kVtBytes, gtid, rv);
-        if (i + 1 < n_kv) load_v8(vp + (size_t)(i + 1) * kRows * kD, tile_rows(i + 1), gtid, rv);
+  };
+  // Loads issued at the start of step i: K_{i+2} and V_{i+1}; returns the
+  // number of load instructions this thread issued (wave-uniform).
+  auto issue_step = [&](int i) -> int {
+    int n = 0;
+    if (grp == 0) {
+      if (i + 2 < n_kv) {
+        issue(false, i + 2);
+        n += 2;
       }
-      mma(i >= 1 && i - 1 < wt, i - 1, i < wt, i);
-      __syncthreads();
+      if (i + 1 < n_kv) {
+        issue(true, i + 1);
+        n += 2;
+      }
+    }
+    return n;
+  };
+
+  // Prologue: K_0 (read first), then K_1 and V_0 (the loads of "step -1").
+  if (grp == 0 && 0 < n_kv) issue(false, 0);
+  dma_barrier(issue_step(-1));  // K_0 has landed
+
+  // Step i = phase A, barrier Y_i, phase B (the schedule of the 16-bit
+  // kernel):
+  //   group 0: A = O(i-1), S(i), loads K_{i+2}, V_{i+1}   B = softmax(i)
+  //   group 1: A = softmax(i-1)                           B = O(i-1), S(i)
+  // Y_i waits for the loads issued in step i - 1 (K_{i+1}, V_i). Between Y_i
+  // and Y_{i+1} the waves read K_i, K_{i+1}, V_{i-1} and V_i, while the loads
+  // in flight write K_{i+2}, K_{i+3}, V_{i+1} and V_{i+2}: distinct slots.
+  if (grp == 0) {
+    for (int i = 0; i <= n_kv; ++i) {
+      const bool do_o = i >= 1 && i - 1 < wt, do_s = i < wt;
+      const bool has_k = i + 2 < n_kv, has_v = i + 1 < n_kv;
+      const int n_new = 2 * has_k + 2 * has_v;
+      if (do_o && do_s) {
+        // full phase: with full tiles the loads are spread over its MFMAs
+        const bool spread = (!has_k || Nk - (i + 2) * kRows >= kRows) && (!has_v || Nk - (i + 1) * kRows >= kRows);
+        if (!spread) issue_step(i);
+        const DmaSpread ex{kp + (size_t)(i + 2) * kRows * kD, vp + (size_t)(i + 1) * kRows * kD,
+                           lds_k + (uint32_t)(((i + 2) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
+                           lds_v + (uint32_t)(((i + 1) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
+                           has_k && spread, has_v && spread, dk, dv};
+        mma_t(std::true_type{}, std::true_type{}, i - 1, i, ex);
+      } else {
+        issue_step(i);
+        mma(do_o, i - 1, do_s, i);
+      }
+      dma_barrier(n_new);  // Y_i
       if (i < wt) softmax(i);
-      __syncthreads();
     }
   } else {
-    u32x4 rk[2];
-    if (n_kv > 0) {
-      load_k8(kp, tile_rows(0), gtid, rk);
-      store_k8(kring, gtid, rk);
-    }
-    __syncthreads();
     for (int i = 0; i <= n_kv; ++i) {
-      if (i + 1 < n_kv) load_k8(kp + (size_t)(i + 1) * kRows * kD, tile_rows(i + 1), gtid, rk);
+      const int n_new = issue_step(i);
       if (i >= 1 && i - 1 < wt) softmax(i - 1);
-      __syncthreads();
+      dma_barrier(n_new);  // Y_i
       mma(i >= 1 && i - 1 < wt, i - 1, i < wt, i);
-      if (i + 1 < n_kv) store_k8(kring + ((i + 1) & 1) * kKBytes, gtid, rk);
-      __syncthreads();
     }
   }
 
