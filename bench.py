@@ -367,6 +367,60 @@ def cpu_baseline_prefill(name="llama3_8b_gqa_n8192", heads=32, fp8=False):
                       f"all 8192 query rows each (float64 NumPy, score matrix materialised); {elapsed:.1f}s"}
 
 
+def cpu_baseline_full(name, causal):
+    """The oracle on every (batch, q-head) of a small prefill workload (all
+    rows, all keys): TFLOP/s by the GPU's FLOP convention."""
+    import oracle
+    c = ai.CONFIGS[name]
+    B, Hq, N, d, dt, grp = c["B"], c["Hq"], c["N"], c["d"], c["dtype"], c["Hq"] // c["Hkv"]
+    scale = 1.0 / math.sqrt(d)
+    elapsed = 0.0
+    for b in range(B):
+        for h in range(Hq):
+            q = ai.bits_to_f64(ai.slab(c["seed"], ai.Q_ID, b, h, N, d, dt), dt)
+            k = ai.bits_to_f64(ai.slab(c["seed"], ai.K_ID, b, h // grp, N, d, dt), dt)
+            v = ai.bits_to_f64(ai.slab(c["seed"], ai.V_ID, b, h // grp, N, d, dt), dt)
+            t0 = time.perf_counter()
+            oracle.attention_head(q, k, v, scale, causal=causal)
+            elapsed += time.perf_counter() - t0
+    flops = prefill_flops(B, Hq, N, N, d, causal)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cpu_cores_used(), "kind": "oracle",
+            "sample": f"the whole workload ({B} x {Hq} heads, N={N}, causal={causal}; float64 NumPy, score matrix "
+                      f"materialised); {elapsed:.1f}s"}
+
+
+def cpu_baseline_sampled(name="llama3_8b_gqa_n131072"):
+    """The oracle on the sampled query rows of every q-head of the long-context
+    workload (each row against all of its visible keys): TFLOP/s by the GPU's
+    FLOP convention over the sampled rows, and the full layer's time at that
+    rate."""
+    import oracle
+    c = ai.CONFIGS[name]
+    Hq, N, d, dt, grp, count = c["Hq"], c["N"], c["d"], c["dtype"], c["Hq"] // c["Hkv"], c["sample_rows"]
+    scale = 1.0 / math.sqrt(d)
+    elapsed = 0.0
+    flops = 0.0
+    kv = {}
+    for h in range(Hq):
+        g = h // grp
+        if g not in kv:
+            kv = {g: (ai.bits_to_f64(ai.slab(c["seed"], ai.K_ID, 0, g, N, d, dt), dt),
+                      ai.bits_to_f64(ai.slab(c["seed"], ai.V_ID, 0, g, N, d, dt), dt))}
+        k, v = kv[g]
+        rows = ai.sample_rows(c["seed"], h, N, count)
+        q = ai.bits_to_f64(ai.slab(c["seed"], ai.Q_ID, 0, h, N, d, dt)[rows], dt)
+        t0 = time.perf_counter()
+        oracle.attention_rows(q, rows, k, v, scale, True, N)
+        elapsed += time.perf_counter() - t0
+        flops += 4.0 * d * float(np.sum(rows + 1))  # row r sees keys 0..r
+    rate = flops / elapsed
+    full_s = prefill_flops(1, Hq, N, N, d, True) / rate
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": cpu_cores_used(), "kind": "oracle",
+            "sample": f"{count} sampled query rows of each of the {Hq} q-heads against all their visible keys "
+                      f"(float64 NumPy); {elapsed:.1f}s; the whole N={N} layer would take about {full_s:.0f}s "
+                      "at this rate (extrapolated)"}
+
+
 def cpu_baseline_backward(name="llama3_8b_gqa_n8192", heads=4):
     """The gradient oracle on `heads` q-heads (one kv-head group) of the
     backward workload, all rows and keys, causal: TFLOP/s by the GPU's FLOP
@@ -580,6 +634,10 @@ def main():
             out["cpu_baseline"] = cpu_baseline_backward()
         elif cfg == "llama3_8b_gqa_n8192_fp8":
             out["cpu_baseline"] = cpu_baseline_prefill(fp8=True)
+        elif pre is not None and pname == "llama3_8b_gqa_n131072":
+            out["cpu_baseline"] = cpu_baseline_sampled()
+        elif pre is not None and pname in ("mha_n4096_fp16", "tiny_mha_n128"):
+            out["cpu_baseline"] = cpu_baseline_full(pname, causal)
         elif pre is not None and pname == "llama3_8b_gqa_n8192":
             out["cpu_baseline"] = cpu_baseline_prefill()
             if dec is not None:
