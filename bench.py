@@ -51,9 +51,9 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "exact_tiled_attention_fwd_amd", "csrc")
 KERNEL_SOURCES = [os.path.join(CSRC, f)
-                  for f in ("fa_tile.h", "fa_fwd.hip", "fa_fwd_d128.hip", "fa_decode.hip", "fa_launch.h", "fa_api.cpp")]
+                  for f in ("fa_tile.h", "fa_fwd.hip", "fa_decode.hip", "fa_launch.h", "fa_api.cpp")]
 # The device code behind each measured kernel (its counter summary records these).
-FWD_D128_SOURCES = ("fa_fwd_d128.hip", "fa_tile.h", "fa_launch.h")
+FWD_SOURCES = ("fa_fwd.hip", "fa_tile.h", "fa_launch.h")
 DECODE_SOURCES = ("fa_decode.hip", "fa_tile.h", "fa_launch.h")
 BWD_SOURCES = ("fa_bwd.hip", "fa_bwd_launch.h", "fa_tile.h", "fa_launch.h")
 FP8_SOURCES = ("fa_fwd_fp8.hip", "fa_fp8_launch.h", "fa_tile.h", "fa_launch.h")
@@ -108,7 +108,10 @@ def counter_traffic(name):
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m_files or not m_src or not m_b:
         return None
-    if m_src.group(1) != kernel_source_hash(m_files.group(1).split()):
+    try:
+        if m_src.group(1) != kernel_source_hash(m_files.group(1).split()):
+            return None
+    except OSError:  # a source the summary names no longer exists
         return None
     return float(m_b.group(1))
 

@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libfa.so")
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_d128.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fwd_fp8.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip", "fa_bwd.hip", "fa_fwd_fp8.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

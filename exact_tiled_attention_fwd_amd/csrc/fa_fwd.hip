@@ -1,22 +1,20 @@
-// fa_fwd.hip - prefill attention forward for gfx950.
+// fa_fwd.hip - prefill attention forward for gfx950, head width 128 or 64.
 //
-// One workgroup owns BM = 256 query rows of one (batch, q-head): 8 waves of 32
-// rows each, in two groups of 4. The workgroup walks the key/value tiles of
-// its kv-head (an outer loop over query blocks and an inner loop over
-// key/value blocks, as in "Implementation details" of "Flash Attention:
-// Revolutionizing Transformer Efficiency", unite.ai). Per tile and wave:
-//   MA: S^T = K Q^T on the matrix cores (fp32 accumulate),
-//   SM: online softmax in base 2 (running max m, running sum l; the merge
-//       identity of "The math of Flash Attention" on the same page),
-//   MB: O^T += V^T P^T with P rounded to the input type.
-// The two groups run out of phase: while one group's waves issue matrix-core
-// work (MB of the previous tile and MA of the current one), the other group's
-// waves, which share the same SIMDs, run their softmax on the vector ALUs.
-// Each phase ends at a workgroup barrier. Group 0 streams the V tiles and
-// group 1 the K tiles HBM -> registers -> LDS, one tile ahead, into a 2-deep
-// ring for each. O is divided by l once after the last tile and written
-// once, with the natural-log LSE. Causal key tiles entirely above the
-// diagonal are never loaded (SDPA page, devhandbook.co.kr, Example 3).
+// One workgroup owns 256 query rows of one (batch, q-head): 8 waves of 32
+// rows in two groups of 4 that alternate between matrix-core phases and
+// online-softmax phases, Q-outer and K/V-inner ("Implementation details",
+// "Flash Attention: Revolutionizing Transformer Efficiency", unite.ai; the
+// merge identity of "The math of Flash Attention" on the same page). Key
+// tiles are 16 KiB: 64 keys at d = 128, 128 keys at d = 64.
+//
+// The waves of one group move each K and V tile HBM -> LDS directly
+// (global_load_lds_dwordx4: no staging registers, no LDS store instructions,
+// no vector-ALU work), into 4-slot rings issued two tiles (K) and one tile
+// (V) ahead of the step that reads them; the fourth slot lets one barrier per
+// step order both the loads and the reuse of slots. V stays row-major in LDS
+// and is read transposed (ds_read_b64_tr_b16) as the A operand of
+// O^T += V^T P^T, so no lane shuffles are needed anywhere. The vector ALUs are
+// left to the softmax.
 #include "fa_launch.h"
 #include "fa_tile.h"
 
@@ -24,19 +22,144 @@ namespace fa {
 
 namespace {
 
-constexpr int kBM = kFwdBlockRows;  // query rows per workgroup
-constexpr int kThreads = 512;  // 8 waves = 2 groups of 4
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kBM = kFwdBlockRows;  // 256 query rows per workgroup
+constexpr int kThreads = 512;       // 8 waves = 2 groups of 4
+constexpr int kSlots = 4;           // ring depth for K and for V
+
+// Tile geometry for head width D: 16 KiB K or V tiles (64 keys at D = 128,
+// 128 keys at D = 64), D / 8 chunks of 16 bytes per row, 256 / (D / 8) rows
+// per block of 256 chunk positions (one load instruction of each of the 4
+// loading waves).
+template <int D>
+struct Geo {
+  static constexpr int ROWS = 8192 / D;
+  static constexpr int CPR = D / 8;
+  static constexpr int RPI = 256 / CPR;
+  static constexpr int TILE = ROWS * D * 2;
+};
+
+// LDS layouts, row-major [ROWS][D] 16-bit:
+//   D = 128 (256-byte rows, 16 chunks): K chunk c of row r at c ^ (r % 16),
+//     so the 16 rows of a quarter-wave A-operand fetch of one chunk column
+//     land on distinct banks; V chunk c at c ^ 4 (r % 4), conflict-free
+//     transposed reads (a half-wave reads 4 rows x 4 chunks).
+//   D = 64 (128-byte rows, 8 chunks; rows r and r + 2 share banks): K chunk
+//     c at c ^ ((r / 2) % 8); V chunk c at c ^ 4 ((r / 2) % 2), which puts the
+//     4 rows x 4 chunks of a half-wave transposed read on distinct banks.
+template <int D>
+__device__ inline int k_phys(int row, int c) {
+  return D == 128 ? c ^ (row & 15) : c ^ ((row >> 1) & 7);
+}
+template <int D>
+__device__ inline int v_phys(int row, int c) {
+  return D == 128 ? c ^ (4 * (row & 3)) : c ^ (4 * ((row >> 1) & 1));
+}
+
+// Byte offset in the global tile (rows rsb bytes apart) of the 16-byte chunk
+// that load instruction i (0..3) of wave w (0..3 of the loading group)
+// writes to LDS position p = 256 i + 64 w + lane (row p / CPR, position
+// p % CPR). The swizzles are involutions, so position -> chunk uses the same
+// map. Rows at or beyond nvalid re-read row nvalid - 1: their scores are
+// masked to -inf and contribute exactly 0. For a full tile the offset of
+// instruction i is that of instruction 0 plus RPI i rows (the swizzles depend
+// on the row only through row % 16), so one offset register serves all four.
+template <int D, bool IS_V>
+__device__ inline uint32_t dma_src(int i, int w, int lane, int nvalid, uint32_t rsb) {
+  constexpr int CPR = Geo<D>::CPR;
+  const int p = 256 * i + 64 * w + lane;
+  const int row = p / CPR, pos = p % CPR;
+  const int c = IS_V ? v_phys<D>(row, pos) : k_phys<D>(row, pos);
+  return (uint32_t)min(row, nvalid - 1) * rsb + (uint32_t)(c * 16);
+}
+
+// One 1 KiB direct-to-LDS load: lane l's 16 bytes from sbase + voff land at
+// LDS address lds + 16 l. Written as asm so that the compiler's wait
+// insertion, which cannot tell the ring slots apart, does not wait for every
+// load in flight before each LDS read; the phase barriers do the waiting.
+__device__ __attribute__((always_inline)) inline void dma16(const uint16_t* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+// Barrier that first waits until this thread has at most `pending` (0, 4 or
+// 8, wave-uniform) direct-to-LDS loads outstanding. No release fence: it
+// would also wait for the loads that are meant to stay in flight.
+__device__ __attribute__((always_inline)) inline void dma_barrier(int pending) {
+  if (pending >= 8)
+    __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+  else if (pending >= 4)
+    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Operand reader of the layouts above. K: one 16-byte read per lane (row
+// 32 kb + lane % 32, chunk 2 ks + lane / 32). V^T: two transposed reads; lane
+// l gets V[16 G + 8 p + 4 h + e][32 mt + l % 32] for e = 0..3, p = 0, 1
+// (h = l / 32), which is the key order of the P accumulator.
+template <int D>
+struct DmaReader {
+  static constexpr int VT_READS = 2;
+  static constexpr bool INTERLEAVE = true;  // transposed reads are slower per wave: spread them
+  __device__ static inline u32x4 k(const char* __restrict__ kl, int kb, int ks, int lane) {
+    const int row = 32 * kb + (lane & 31);
+    return *reinterpret_cast<const u32x4*>(kl + row * (2 * D) + k_phys<D>(row, 2 * ks + (lane >> 5)) * 16);
+  }
+  __device__ static inline u32x4 vt(const char* __restrict__ vl, int mt, int G, int lane) {
+    const int gi = lane >> 4, e = (lane >> 2) & 3, qq = lane & 3;
+    const int h = gi >> 1, dh = gi & 1;
+    const int c = 4 * mt + 2 * dh + (qq >> 1);
+    u32x4 out;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int row = 16 * G + 8 * p + 4 * h + e;
+      const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(vl + row * (2 * D) + v_phys<D>(row, c) * 16 + 8 * (qq & 1)));
+      const u32x2 w = __builtin_bit_cast(u32x2, t);
+      out[2 * p] = w[0];
+      out[2 * p + 1] = w[1];
+    }
+    return out;
+  }
+};
+
+// The 8 tile loads of one step, slotted in after MFMAs 2, 6, ..., 30 of a
+// 32-op matrix-core phase, so that the loads of the four loading waves reach
+// the address unit a few at a time instead of in one burst. Full tiles only.
+struct DmaSpread {
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  uint32_t kslot, vslot;
+  bool has_k, has_v;
+  uint32_t dk, dv;
+  long long kstep, vstep;  // RPI rows, in elements
+  __device__ __attribute__((always_inline)) void operator()(int t) const {
+    if ((t & 3) != 2) return;
+    const int j = t >> 2;
+    if (j < 4) {
+      if (has_k) dma16(kbase + kstep * j, dk, kslot + 4096 * j);
+    } else {
+      if (has_v) dma16(vbase + vstep * (j - 4), dv, vslot + 4096 * (j - 4));
+    }
+  }
+};
 
 template <int DT, int D, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Nq_all, int Nk_all,
     float scale_log2, int n_qt, Varlen vlen, Layout ly) {
-  constexpr int ROWS = 8192 / D;  // keys per tile: 64 (d=128) or 128 (d=64)
-  using T = Tile<D, ROWS>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * T::K_BYTES + 2 * T::VT_BYTES];
-  char* const kring = smem;                    // K tiles, slot = tile & 1
-  char* const vring = smem + 2 * T::K_BYTES;   // V^T tiles, slot = tile & 1
+  constexpr int ROWS = Geo<D>::ROWS, kTile = Geo<D>::TILE, RPI = Geo<D>::RPI;
+  constexpr int KS = D / 16, KB = ROWS / 32, MT = D / 32;
+  using Rd = DmaReader<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kSlots * kTile];
+  char* const kring = smem;                   // K tile t in slot t % 4
+  char* const vring = smem + kSlots * kTile;  // V tile t in slot t % 4
 
   const Work wk = VARLEN ? map_work_packed(blockIdx.x, B, Hq, Hkv, n_qt) : map_work(blockIdx.x, B, Hq, Hkv, n_qt);
   const Slabs sl = slabs_of<VARLEN>(wk, q, k, v, o, lse, Hq, Nq_all, Nk_all, vlen, ly);
@@ -44,8 +167,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
   const int q0 = wk.qt * kBM;
   if (VARLEN && q0 >= Nq) return;  // past this sequence's rows (the whole workgroup)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
-  const int grp = wave >> 2;                // 0: V loader, MFMA first; 1: K loader
-  const int gtid = threadIdx.x & 255;       // thread index within the group
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int grp = wave >> 2;  // 0: matrix cores first; 1: softmax first
   const int q0w = q0 + 32 * wave;  // first query row of this wave
   const int off = Nk - Nq;         // causal: key j visible to query i iff j <= i + off
 
@@ -53,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
   const uint16_t* kp = sl.k;
   const uint16_t* vp = sl.v;
 
-  // Key tiles this workgroup visits.
+  // Key tiles this workgroup visits (none for rows that see no key).
   int n_kv = (Nk + ROWS - 1) / ROWS;
   if (CAUSAL) {
     const int last_key = min(q0 + kBM, Nq) - 1 + off;
@@ -69,24 +192,27 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
 
   // Q^T operand (B operand of S^T = K Q^T), held for the whole loop.
   const int qrow = q0w + (lane & 31);
-  u32x4 qop[T::KS];
+  u32x4 qop[KS];
 #pragma unroll
-  for (int ks = 0; ks < T::KS; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     if (qrow < Nq)
       qop[ks] = *reinterpret_cast<const u32x4*>(qp + (size_t)qrow * sl.qs + 16 * ks + 8 * half);
     else
       qop[ks] = u32x4{0u, 0u, 0u, 0u};
   }
+  // Wait for Q here, once: the tile loads are asm the compiler does not count,
+  // so a Q wait it placed inside the loop would also wait for them.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-  f32x16 acc_o[T::MT];
+  f32x16 acc_o[MT];
 #pragma unroll
-  for (int mt = 0; mt < T::MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[mt][r] = 0.f;
   float m_run = -__builtin_inff();  // row reference point, log2 units
   float l_run = 0.f;                // this lane's share of the running sum
-  f32x16 s[T::KB];                  // S^T of the tile last multiplied
-  uint32_t pk[T::KB][8];            // P of the tile last softmaxed
+  f32x16 s[KB];                     // S^T of the tile last multiplied
+  uint32_t pk[KB][8];               // P of the tile last softmaxed
 
   // SM(j): mask the ragged key tail / causal diagonal, online softmax -> pk.
   auto softmax = [&](int j) {
@@ -95,77 +221,125 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
     if (need_mask) {
       const int lim = CAUSAL ? min(Nk, qrow + off + 1) : Nk;  // keys < lim are visible
 #pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (j0 + 32 * kb + acc_key(r, half) >= lim) s[kb][r] = -__builtin_inff();
     }
-    softmax_step<DT, T::KB, T::MT>(s, scale_log2, m_run, l_run, acc_o, pk);
+    softmax_step<DT, KB, MT>(s, scale_log2, m_run, l_run, acc_o, pk);
   };
   // Matrix-core phase: MB(jo) = O^T += V^T_jo P^T (if do_o), MA(js) = S^T = K_js Q^T (if do_s).
   // mma_pre issues the first operand reads; mma finishes the phase.
   u32x4 obuf[kPF];
   auto mma_pre = [&](bool do_o, int jo, bool do_s, int js) {
-    const char* vl = vring + (jo & 1) * T::VT_BYTES;
-    const char* kl = kring + (js & 1) * T::K_BYTES;
+    const char* vl = vring + (jo % kSlots) * kTile;
+    const char* kl = kring + (js % kSlots) * kTile;
     if (do_o && do_s)
-      mma_prefetch<D, ROWS, true, true>(obuf, vl, kl, lane);
+      mma_prefetch<D, ROWS, true, true, Rd>(obuf, vl, kl, lane);
     else if (do_o)
-      mma_prefetch<D, ROWS, true, false>(obuf, vl, kl, lane);
+      mma_prefetch<D, ROWS, true, false, Rd>(obuf, vl, kl, lane);
     else if (do_s)
-      mma_prefetch<D, ROWS, false, true>(obuf, vl, kl, lane);
+      mma_prefetch<D, ROWS, false, true, Rd>(obuf, vl, kl, lane);
   };
   auto mma = [&](bool do_o, int jo, bool do_s, int js) {
-    const char* vl = vring + (jo & 1) * T::VT_BYTES;
-    const char* kl = kring + (js & 1) * T::K_BYTES;
+    const char* vl = vring + (jo % kSlots) * kTile;
+    const char* kl = kring + (js % kSlots) * kTile;
     if (do_o && do_s)
-      mma_run<DT, D, ROWS, true, true>(obuf, vl, kl, pk, qop, acc_o, s, lane);
+      mma_run<DT, D, ROWS, true, true, Rd>(obuf, vl, kl, pk, qop, acc_o, s, lane);
     else if (do_o)
-      mma_run<DT, D, ROWS, true, false>(obuf, vl, kl, pk, qop, acc_o, s, lane);
+      mma_run<DT, D, ROWS, true, false, Rd>(obuf, vl, kl, pk, qop, acc_o, s, lane);
     else if (do_s)
-      mma_run<DT, D, ROWS, false, true>(obuf, vl, kl, pk, qop, acc_o, s, lane);
+      mma_run<DT, D, ROWS, false, true, Rd>(obuf, vl, kl, pk, qop, acc_o, s, lane);
   };
-  auto tile_rows = [&](int j) { return min(ROWS, Nk - j * ROWS); };
 
-  // Each group runs its own loop (both execute the same number of barriers):
-  // macro-step i is phase A then phase B, each closed by a barrier.
-  //   group 0: A = store V_i, load V_{i+1}, MB(i-1), MA(i)   B = SM(i)
-  //   group 1: A = load K_{i+1}, SM(i-1)                     B = MB(i-1), MA(i), store K_{i+1}
-  // V_i / K_i live in ring slot i & 1; a slot is rewritten only after the
-  // barrier that ends the last phase reading its previous tile.
-  if (grp == 0) {
-    u32x4 rv[T::U][4];
-    load_v<D, ROWS>(vp, sl.vs, tile_rows(0), gtid, rv);
-    store_v<D, ROWS>(vring, gtid, rv);
-    if (n_kv > 1) load_v<D, ROWS>(vp + (size_t)ROWS * sl.vs, sl.vs, tile_rows(1), gtid, rv);
-    __syncthreads();
-    mma_pre(false, -1, 0 < wave_tiles, 0);
-    for (int i = 0; i <= n_kv; ++i) {
-      if (i >= 1 && i < n_kv) {
-        store_v<D, ROWS>(vring + (i & 1) * T::VT_BYTES, gtid, rv);
-        if (i + 1 < n_kv) load_v<D, ROWS>(vp + (size_t)(i + 1) * ROWS * sl.vs, sl.vs, tile_rows(i + 1), gtid, rv);
+  // ---- direct-to-LDS tile loads, issued by the waves of group 0 only (they
+  // wait at the Y barrier anyway): 4 instructions per wave per tile.
+  const uint32_t lds_k = (uint32_t)(uintptr_t)(lds_void_t*)kring;
+  const uint32_t lds_v = (uint32_t)(uintptr_t)(lds_void_t*)vring;
+  const int wg = wv & 3;  // wave index within its group
+  const uint32_t ksb = 2u * (uint32_t)sl.ks, vsb = 2u * (uint32_t)sl.vs;  // row strides in bytes
+  const uint32_t dk = dma_src<D, false>(0, wg, lane, ROWS, ksb);  // source offsets of a full tile
+  const uint32_t dv = dma_src<D, true>(0, wg, lane, ROWS, vsb);
+  const long long kstep = (long long)RPI * sl.ks, vstep = (long long)RPI * sl.vs;
+  auto issue = [&](bool is_v, int t) {
+    const int nvalid = min(ROWS, Nk - t * ROWS);
+    const uint16_t* base = is_v ? vp + (long long)t * ROWS * sl.vs : kp + (long long)t * ROWS * sl.ks;
+    const uint32_t slot = (is_v ? lds_v : lds_k) + (uint32_t)((t % kSlots) * kTile) + (uint32_t)(64 * wg * 16);
+    if (nvalid == ROWS) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma16(base + (is_v ? vstep : kstep) * i, is_v ? dv : dk, slot + 4096 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dma16(base, is_v ? dma_src<D, true>(i, wg, lane, nvalid, vsb) : dma_src<D, false>(i, wg, lane, nvalid, ksb),
+              slot + 4096 * i);
+    }
+  };
+  // Loads issued at the start of step i: K_{i+2} and V_{i+1}; returns the
+  // number of load instructions this thread issued (wave-uniform).
+  auto issue_step = [&](int i) -> int {
+    int n = 0;
+    if (grp == 0) {
+      if (i + 2 < n_kv) {
+        issue(false, i + 2);
+        n += 4;
       }
-      mma(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
-      __syncthreads();
+      if (i + 1 < n_kv) {
+        issue(true, i + 1);
+        n += 4;
+      }
+    }
+    return n;
+  };
+
+  // Prologue: K_0 (read first), then K_1 and V_0 (the loads of "step -1").
+  if (grp == 0 && 0 < n_kv) issue(false, 0);
+  dma_barrier(issue_step(-1));  // K_0 has landed
+
+  // Step i = phase A, barrier Y_i, phase B; Y_i is the step's only barrier:
+  //   group 0: A = MB(i-1), MA(i), loads K_{i+2}, V_{i+1}   B = SM(i), first reads of MB(i), MA(i+1)
+  //   group 1: A = SM(i-1), first reads of MB(i-1), MA(i)  B = MB(i-1), MA(i)
+  // Y_i waits for the loads issued in step i - 1 (K_{i+1}, V_i). Between Y_i
+  // and Y_{i+1} the waves read K_i, K_{i+1}, V_{i-1} and V_i, while the loads
+  // in flight write K_{i+2}, K_{i+3}, V_{i+1} and V_{i+2}: distinct slots of
+  // the 4-slot rings. A slot is rewritten only after the barrier that follows
+  // the MFMAs consuming its last reads.
+  if (grp == 0) {
+    mma_pre(false, 0, 0 < wave_tiles, 0);
+    for (int i = 0; i <= n_kv; ++i) {
+      const bool do_o = i >= 1 && i - 1 < wave_tiles, do_s = i < wave_tiles;
+      const bool has_k = i + 2 < n_kv, has_v = i + 1 < n_kv;
+      const int n_new = 4 * has_k + 4 * has_v;
+      if (do_o && do_s) {
+        // full phase: with full tiles the loads are spread over its MFMAs
+        const bool spread = (!has_k || Nk - (i + 2) * ROWS >= ROWS) && (!has_v || Nk - (i + 1) * ROWS >= ROWS);
+        if (!spread) issue_step(i);
+        const DmaSpread ex{kp + (long long)(i + 2) * ROWS * sl.ks, vp + (long long)(i + 1) * ROWS * sl.vs,
+                           lds_k + (uint32_t)(((i + 2) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
+                           lds_v + (uint32_t)(((i + 1) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
+                           has_k && spread, has_v && spread, dk, dv, kstep, vstep};
+        mma_run<DT, D, ROWS, true, true, Rd>(obuf, vring + ((i - 1) % kSlots) * kTile,
+                                                    kring + (i % kSlots) * kTile, pk, qop, acc_o, s, lane, ex);
+      } else {
+        issue_step(i);
+        if (do_o)
+          mma_run<DT, D, ROWS, true, false, Rd>(obuf, vring + ((i - 1) % kSlots) * kTile,
+                                                       kring + (i % kSlots) * kTile, pk, qop, acc_o, s, lane);
+        else if (do_s)
+          mma_run<DT, D, ROWS, false, true, Rd>(obuf, vring, kring + (i % kSlots) * kTile, pk, qop, acc_o,
+                                                       s, lane);
+      }
+      dma_barrier(n_new);  // Y_i
       if (i < wave_tiles) softmax(i);
-      // V_i (stored in phase A) is complete: start the next phase's reads.
       mma_pre(i < wave_tiles, i, i + 1 < wave_tiles, i + 1);
-      __syncthreads();
     }
   } else {
-    u32x4 rk[TileRegs<D, ROWS>::KU];
-    load_k<D, ROWS>(kp, sl.ks, tile_rows(0), gtid, rk);
-    store_k<D, ROWS>(kring, gtid, rk);
-    __syncthreads();
     for (int i = 0; i <= n_kv; ++i) {
-      if (i + 1 < n_kv) load_k<D, ROWS>(kp + (size_t)(i + 1) * ROWS * sl.ks, sl.ks, tile_rows(i + 1), gtid, rk);
+      const int n_new = issue_step(i);
       if (i >= 1 && i - 1 < wave_tiles) softmax(i - 1);
-      // V_{i-1} and K_i were completed before the last barrier.
       mma_pre(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
-      __syncthreads();
+      dma_barrier(n_new);  // Y_i
       mma(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
-      if (i + 1 < n_kv) store_k<D, ROWS>(kring + ((i + 1) & 1) * T::K_BYTES, gtid, rk);
-      __syncthreads();
     }
   }
 
@@ -176,7 +350,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
   if (qrow < Nq) {
     uint16_t* orow = sl.o + (size_t)qrow * sl.os;
 #pragma unroll
-    for (int mt = 0; mt < T::MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d0 = 32 * mt + 8 * i + 4 * half;
@@ -190,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
 }
 
 template <int DT, int D, bool CAUSAL, bool VARLEN>
-hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   const int rows = VARLEN ? a.max_seqlen_q : a.Nq;
   const int n_qt = (rows + kBM - 1) / kBM;
   const long long nblocks = (long long)n_qt * a.B * a.Hq;
@@ -203,20 +377,22 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int DT, bool CAUSAL>
-hipError_t launch_fwd_v(const FwdArgs& a, hipStream_t stream) {
-  return a.cu_q != nullptr ? launch_fwd_t<DT, 64, CAUSAL, true>(a, stream)
-                           : launch_fwd_t<DT, 64, CAUSAL, false>(a, stream);
+template <int DT, int D, bool CAUSAL>
+hipError_t launch_v(const FwdArgs& a, hipStream_t stream) {
+  return a.cu_q != nullptr ? launch_t<DT, D, CAUSAL, true>(a, stream) : launch_t<DT, D, CAUSAL, false>(a, stream);
+}
+
+template <int D>
+hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
+  const bool c = a.causal != 0;
+  if (a.dtype == DT_BF16) return c ? launch_v<DT_BF16, D, true>(a, stream) : launch_v<DT_BF16, D, false>(a, stream);
+  return c ? launch_v<DT_FP16, D, true>(a, stream) : launch_v<DT_FP16, D, false>(a, stream);
 }
 
 }  // namespace
 
-// d = 128 runs the direct-to-LDS kernel; d = 64 the register-staged one.
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-  if (a.d == 128) return launch_fwd_d128(a, stream);
-  const bool c = a.causal != 0;
-  if (a.dtype == DT_BF16) return c ? launch_fwd_v<DT_BF16, true>(a, stream) : launch_fwd_v<DT_BF16, false>(a, stream);
-  return c ? launch_fwd_v<DT_FP16, true>(a, stream) : launch_fwd_v<DT_FP16, false>(a, stream);
+  return a.d == 128 ? launch_d<128>(a, stream) : launch_d<64>(a, stream);
 }
 
 }  // namespace fa

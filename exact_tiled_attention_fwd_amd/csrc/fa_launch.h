@@ -70,7 +70,6 @@ constexpr int kDecodeTileRows = 128;
 constexpr int kFwdBlockRows = 256;  // query rows per prefill workgroup
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
-hipError_t launch_fwd_d128(const FwdArgs& a, hipStream_t stream);  // d = 128 only
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace fa

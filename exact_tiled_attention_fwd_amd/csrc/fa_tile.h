@@ -1,6 +1,6 @@
 // fa_tile.h - gfx950 device building blocks shared by the prefill and decode
-// kernels: HBM->register->LDS tile movement, matrix-core (MFMA) operand
-// fetches, and the online-softmax step.
+// kernels: the matrix-core (MFMA) phase of a tile pair, the online-softmax
+// step, the per-lane reductions and the prefill work order.
 //
 // The arithmetic follows "Flash Attention: Revolutionizing Transformer
 // Efficiency" (unite.ai), sections "The math of Flash Attention" (subtract the
@@ -16,8 +16,8 @@
 // The S^T accumulator holds, in lane l, query column l%32 and 16 keys, so the
 // per-query max and sum are lane-local up to one exchange with lane l^32, and
 // the accumulator registers are already the B operand of the second product
-// once rounded to 16 bits. V is transposed while it is written to LDS, with the
-// keys of each 16-key group stored in the order the accumulator holds them.
+// once rounded to 16 bits; the V^T operand is gathered from row-major V with
+// transposed LDS reads in the key order of that accumulator.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,163 +40,15 @@ enum { DT_BF16 = 0, DT_FP16 = 1 };
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Geometry of one K/V tile of ROWS keys and head width D, as laid out in LDS.
-//   K   : row-major [ROWS][D] 16-bit, 16-byte chunks XOR-swizzled per row so
-//         that the 32 rows an MFMA operand fetch touches hit distinct banks.
-//   V^T : [D][ROWS] 16-bit plus 16 bytes of padding per row; keys permuted
-//         within each group of 16 (see vt_pos).
+// MFMA counts of one tile pair of ROWS keys at head width D.
 template <int D, int ROWS>
 struct Tile {
   static_assert(D == 64 || D == 128, "head width");
-  static_assert(ROWS % 64 == 0, "tile rows");
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per K row
-  static constexpr int KB = ROWS / 32;               // 32-key blocks
-  static constexpr int KS = D / 16;                  // MFMA k-steps over d
-  static constexpr int MT = D / 32;                  // 32-row blocks of O^T
-  static constexpr int K_BYTES = ROWS * D * 2;
-  static constexpr int VT_STRIDE = ROWS * 2 + 16;
-  static constexpr int VT_BYTES = D * VT_STRIDE;
-  static constexpr int STAGE_BYTES = K_BYTES + VT_BYTES;
-  static constexpr int UNITS = (ROWS / 4) * CPR;     // (4 keys x 16 bytes) units
-  static constexpr int U = UNITS / 256;              // units per thread (256 threads)
-  static_assert(UNITS % 256 == 0, "tile/threads");
-
-  __device__ static inline int swz(int row) { return (row / (16 / CPR)) % CPR; }
+  static_assert(ROWS % 32 == 0, "tile rows");
+  static constexpr int KB = ROWS / 32;  // 32-key blocks
+  static constexpr int KS = D / 16;     // MFMA k-steps over d
+  static constexpr int MT = D / 32;     // 32-row blocks of O^T
 };
-
-// ------------------------------------------------------------------ HBM -> regs
-// K moves in 16-byte chunks in row-major order (a wave covers 64 consecutive
-// chunks: fully coalesced loads, and each 16-lane group writes one LDS row).
-// V moves in units of 4 consecutive rows x one 16-byte chunk, which is what
-// the transposed LDS layout needs; within a wave the 64 lanes cover 16
-// row-quads x 4 chunks, which keeps the transposed LDS writes conflict-free.
-template <int D, int ROWS>
-struct TileRegs {
-  static constexpr int KU = ROWS * (D / 8) / 256;  // K chunks per thread
-  u32x4 k[KU];
-  u32x4 v[Tile<D, ROWS>::U][4];
-};
-
-template <int D, int ROWS>
-__device__ inline void k_coords(int tid, int p, int& row, int& c) {
-  constexpr int CPR = D / 8;
-  const int idx = tid + 256 * p;
-  row = idx / CPR;
-  c = idx % CPR;
-}
-
-template <int D, int ROWS>
-__device__ inline void unit_coords(int tid, int p, int& kq, int& c) {
-  constexpr int CG = Tile<D, ROWS>::CPR / 4;  // chunk groups per row
-  const int w = tid >> 6, lane = tid & 63;
-  const int wu = w + 4 * p;
-  kq = 16 * (wu / CG) + (lane & 15);
-  c = 4 * (wu % CG) + (lane >> 4);
-}
-
-// Loads of one tile by a group of 256 threads (tid in [0, 256)); rows are rs
-// elements apart. Rows [0, nvalid) of the tile are valid, nvalid >= 1; rows at or beyond nvalid
-// re-read row nvalid-1: their scores are masked to -inf, so they contribute
-// exactly 0, and no row past the valid range is ever touched.
-template <int D, int ROWS>
-__device__ inline void load_k(const uint16_t* __restrict__ kbase, int rs, int nvalid, int tid,
-                              u32x4 (&rk)[TileRegs<D, ROWS>::KU]) {
-  const bool full = nvalid >= ROWS;
-#pragma unroll
-  for (int p = 0; p < TileRegs<D, ROWS>::KU; ++p) {
-    int row, c;
-    k_coords<D, ROWS>(tid, p, row, c);
-    if (!full) row = min(row, nvalid - 1);
-    rk[p] = *reinterpret_cast<const u32x4*>(kbase + (size_t)row * rs + (size_t)c * 8);
-  }
-}
-
-template <int D, int ROWS>
-__device__ inline void load_v(const uint16_t* __restrict__ vbase, int rs, int nvalid, int tid,
-                              u32x4 (&rv)[Tile<D, ROWS>::U][4]) {
-  const bool full = nvalid >= ROWS;
-#pragma unroll
-  for (int p = 0; p < Tile<D, ROWS>::U; ++p) {
-    int kq, c;
-    unit_coords<D, ROWS>(tid, p, kq, c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int row = 4 * kq + i;
-      if (!full) row = min(row, nvalid - 1);
-      rv[p][i] = *reinterpret_cast<const u32x4*>(vbase + (size_t)row * rs + (size_t)c * 8);
-    }
-  }
-}
-
-// Position (in elements) of key kk (0..15) inside its 16-key group of V^T: the
-// accumulator of S^T holds, in lane half h and element e of an 8-element
-// operand, key 8*(e/4) + 4*h + e%4; V^T stores that key at position 8*h + e,
-// so one 16-byte read per lane yields the matching A operand.
-__device__ inline int vt_quad_pos(int quad) {  // quad = kk/4 in 0..3
-  return (quad == 1) ? 2 : (quad == 2) ? 1 : quad;
-}
-
-// ------------------------------------------------------------------ regs -> LDS
-template <int D, int ROWS>
-__device__ inline void store_k(char* __restrict__ kl, int tid, const u32x4 (&rk)[TileRegs<D, ROWS>::KU]) {
-  using T = Tile<D, ROWS>;
-#pragma unroll
-  for (int p = 0; p < TileRegs<D, ROWS>::KU; ++p) {
-    int row, c;
-    k_coords<D, ROWS>(tid, p, row, c);
-    *reinterpret_cast<u32x4*>(kl + row * (D * 2) + ((c ^ T::swz(row)) * 16)) = rk[p];
-  }
-}
-
-// V^T: each unit covers 8 head-dim rows x the 4 keys of its row-quad (8 bytes).
-template <int D, int ROWS>
-__device__ inline void store_v(char* __restrict__ vl, int tid, const u32x4 (&rv)[Tile<D, ROWS>::U][4]) {
-  using T = Tile<D, ROWS>;
-#pragma unroll
-  for (int p = 0; p < T::U; ++p) {
-    int kq, c;
-    unit_coords<D, ROWS>(tid, p, kq, c);
-    const int grp = kq >> 2;
-    const int pos = 16 * grp + 4 * vt_quad_pos(kq & 3);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint32_t a0 = rv[p][0][t], a1 = rv[p][1][t], a2 = rv[p][2][t], a3 = rv[p][3][t];
-      // element 2t (low halves) and 2t+1 (high halves) of the 4 rows
-      const u32x2 even = {__builtin_amdgcn_perm(a1, a0, 0x05040100u), __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
-      const u32x2 odd = {__builtin_amdgcn_perm(a1, a0, 0x07060302u), __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
-      const int d0 = 8 * c + 2 * t;
-      *reinterpret_cast<u32x2*>(vl + d0 * T::VT_STRIDE + pos * 2) = even;
-      *reinterpret_cast<u32x2*>(vl + (d0 + 1) * T::VT_STRIDE + pos * 2) = odd;
-    }
-  }
-}
-
-// A stage holds K (K_BYTES) followed by V^T (VT_BYTES).
-template <int D, int ROWS>
-__device__ inline void store_tile(char* __restrict__ stage, const TileRegs<D, ROWS>& r) {
-  store_k<D, ROWS>(stage, threadIdx.x, r.k);
-  store_v<D, ROWS>(stage + Tile<D, ROWS>::K_BYTES, threadIdx.x, r.v);
-}
-
-// ------------------------------------------------------------------ operands
-// A operand of S^T = K Q^T: key row 32*kb + lane%32, d = 16*ks + 8*(lane/32) .. +7
-// (kl points at the K region of a stage.)
-template <int D, int ROWS>
-__device__ inline u32x4 k_operand(const char* __restrict__ kl, int kb, int ks, int lane) {
-  using T = Tile<D, ROWS>;
-  const int row = 32 * kb + (lane & 31);
-  const int chunk = 2 * ks + (lane >> 5);
-  return *reinterpret_cast<const u32x4*>(kl + row * (D * 2) + ((chunk ^ T::swz(row)) * 16));
-}
-
-// A operand of O^T += V^T P^T: d row 32*mt + lane%32, 16-key group G, half lane/32
-// (vl points at the V^T region of a stage.)
-template <int D, int ROWS>
-__device__ inline u32x4 vt_operand(const char* __restrict__ vl, int mt, int G, int lane) {
-  using T = Tile<D, ROWS>;
-  const int d = 32 * mt + (lane & 31);
-  return *reinterpret_cast<const u32x4*>(vl + d * T::VT_STRIDE + G * 32 + (lane >> 5) * 16);
-}
 
 // ------------------------------------------------------------------ MFMA
 template <int DT>
@@ -227,21 +79,9 @@ __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 // are already complete), mma_run does the rest.
 constexpr int kPF = 4;
 
-// Operand reader of the register-staged layouts above (K swizzled, V stored
-// transposed): one LDS read per operand.
-template <int D, int ROWS>
-struct StagedReader {
-  static constexpr int VT_READS = 1;  // LDS read instructions per V^T operand
-  static constexpr bool INTERLEAVE = false;
-  __device__ static inline u32x4 k(const char* __restrict__ kl, int kb, int ks, int lane) {
-    return k_operand<D, ROWS>(kl, kb, ks, lane);
-  }
-  __device__ static inline u32x4 vt(const char* __restrict__ vl, int mt, int G, int lane) {
-    return vt_operand<D, ROWS>(vl, mt, G, lane);
-  }
-};
-
-template <int D, int ROWS, bool DO_O, bool DO_S, class RD = StagedReader<D, ROWS>>
+// RD (the operand reader) supplies k(kl, kb, ks, lane) and vt(vl, mt, G, lane),
+// VT_READS (LDS reads per V^T operand) and INTERLEAVE.
+template <int D, int ROWS, bool DO_O, bool DO_S, class RD>
 struct MmaPlan {
   using T = Tile<D, ROWS>;
   static constexpr int NO = DO_O ? T::KB * 2 * T::MT : 0;
@@ -277,7 +117,7 @@ struct MmaPlan {
   }
 };
 
-template <int D, int ROWS, bool DO_O, bool DO_S, class RD = StagedReader<D, ROWS>>
+template <int D, int ROWS, bool DO_O, bool DO_S, class RD>
 __device__ __attribute__((always_inline)) inline void mma_prefetch(u32x4 (&buf)[kPF], const char* __restrict__ vl, const char* __restrict__ kl,
                                     int lane) {
 #pragma unroll
@@ -291,7 +131,7 @@ struct NoExtra {
   __device__ void all() const {}
 };
 
-template <int DT, int D, int ROWS, bool DO_O, bool DO_S, class RD = StagedReader<D, ROWS>, class EX = NoExtra>
+template <int DT, int D, int ROWS, bool DO_O, bool DO_S, class RD, class EX = NoExtra>
 __device__ __attribute__((always_inline)) inline void mma_run(u32x4 (&buf)[kPF], const char* __restrict__ vl, const char* __restrict__ kl,
                                const uint32_t (&pk)[ROWS / 32][8], const u32x4 (&qop)[D / 16],
                                f32x16 (&acc_o)[D / 32], f32x16 (&s)[ROWS / 32], int lane, const EX& ex = EX{}) {
