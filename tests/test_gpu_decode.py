@@ -131,3 +131,41 @@ def test_most_partials_per_pair(fa):
     # middle of the first wave's share; with 384-row shares sequence 1 then
     # gets ceil(1000 / 384) + 1 = 4 partials, the most the workspace holds.
     decode_case(fa, 26, 2, 4, 1, 1000, 64, ai.BF16, [192, 1000], num_splits=3)
+
+
+def _random_cases(n=16, seed=27):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = int(rng.integers(1, 100))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        grp = int(rng.choice([1, 2, 4, 8]))
+        Lcap = int(rng.integers(1, 1500))
+        d = int(rng.choice([64, 128]))
+        dt = ai.BF16 if rng.random() < 0.5 else ai.FP16
+        lens = rng.integers(0, Lcap + 1, B).astype(np.int32)
+        lens[rng.random(B) < 0.1] = 0
+        splits = int(rng.choice([0, 0, 1, 2, 7]))
+        cases.append((100 + i, B, Hkv * grp, Hkv, Lcap, d, dt, lens, splits))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(), ids=lambda c: f"s{c[0]}B{c[1]}Hq{c[2]}Hkv{c[3]}L{c[4]}d{c[5]}{c[6]}n{c[8]}")
+def test_decode_random_shapes(fa, case):
+    # Seeded shapes around the split's edges: many or few sequences, empty
+    # ones, short caches (shares spanning many pairs), explicit split counts.
+    import torch
+    seed, B, Hq, Hkv, Lcap, d, dt, lens, splits = case
+    announce(f"decode random seed={seed} B={B} Hq={Hq} Hkv={Hkv} Lcap={Lcap} d={d} {dt} splits={splits}")
+    x = ai.decode_inputs(seed, B, Hq, Hkv, Lcap, d, dt, lens)
+    q, kc, vc, sl = dev_inputs(x)
+    o, lse = fa.decode(q, kc, vc, sl, num_splits=splits)
+    torch.cuda.synchronize()
+    o_np, l_np = from_dev(o, dt), lse.cpu().numpy()
+    empty = lens == 0
+    assert np.all(o_np[empty] == 0) and np.all(np.isneginf(l_np[empty]))
+    if np.all(empty):
+        return
+    xs = {k: (v[~empty] if k in ("q", "k_cache", "v_cache", "seqlens") else v) for k, v in x.items()}
+    O_ref, L_ref = oracle_decode(xs, 1.0 / math.sqrt(d))
+    compare(o_np[~empty], O_ref, l_np[~empty], L_ref, f"decode random seed {seed}")

@@ -108,3 +108,39 @@ def test_bad_page_entry_poisons_only_its_sequence(fa):
     assert torch.all(torch.isnan(o[1].float())) and torch.all(torch.isnan(lse[1]))
     assert torch.equal(o[0], o_ok[0]) and torch.equal(lse[0], l_ok[0])
     assert torch.equal(o[2], o_ok[2]) and torch.equal(lse[2], l_ok[2])
+
+
+def _random_paged_cases(n=8, seed=29):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = int(rng.integers(1, 80))
+        Hkv = int(rng.choice([1, 2, 8]))
+        grp = int(rng.choice([1, 4]))
+        P = int(rng.choice([32, 64, 128]))
+        Lcap = P * int(rng.integers(1, 20))
+        d = int(rng.choice([64, 128]))
+        dt = ai.BF16 if rng.random() < 0.5 else ai.FP16
+        lens = [int(v) for v in rng.integers(0, Lcap + 1, B)]
+        cases.append((400 + i, B, Hkv * grp, Hkv, Lcap, d, dt, lens, P))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_paged_cases(), ids=lambda c: f"s{c[0]}B{c[1]}Hq{c[2]}L{c[4]}d{c[5]}{c[6]}P{c[8]}")
+def test_paged_decode_random_shapes(fa, case):
+    import torch
+    seed, B, Hq, Hkv, Lcap, d, dt, lens, P = case
+    announce(f"paged decode random seed={seed} B={B} Hq={Hq} Hkv={Hkv} Lcap={Lcap} d={d} {dt} P={P}")
+    x, pl = paged_case(seed, B, Hq, Hkv, Lcap, d, dt, lens, P)
+    q, kp, vp, table, sl = dev_paged(x, pl)
+    o, lse = fa.decode_paged(q, kp, vp, table, sl)
+    torch.cuda.synchronize()
+    empty = np.asarray(lens) == 0
+    o_np, l_np = from_dev(o, dt), lse.cpu().numpy()
+    assert np.all(o_np[empty] == 0) and np.all(np.isneginf(l_np[empty]))
+    if np.all(empty):
+        return
+    f = lambda a: ai.bits_to_f64(a, dt)
+    O_ref, L_ref = oracle.decode_paged(f(x["q"]), f(pl["k_pages"]), f(pl["v_pages"]), pl["block_table"],
+                                       x["seqlens"], 1.0 / math.sqrt(d))
+    compare(o_np[~empty], O_ref[~empty], l_np[~empty], L_ref[~empty], f"paged decode random seed {seed}")
