@@ -177,3 +177,27 @@ def test_lse_optional_and_errors_raise(fa):
         fa.attention(q[..., :32].contiguous(), k[..., :32].contiguous(), v[..., :32].contiguous())
     with pytest.raises(ValueError):
         fa.attention(q, k, v, causal=True, scale=-1.0)
+
+
+def _random_prefill_cases(n=12, seed=31):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        Hq = Hkv * int(rng.choice([1, 2, 4]))
+        B = int(rng.integers(1, 3))
+        Nk = int(rng.integers(1, 1100))
+        causal = bool(rng.random() < 0.6)
+        Nq = int(rng.integers(1, Nk + 1)) if causal else int(rng.integers(1, 1100))
+        dt = ai.BF16 if rng.random() < 0.5 else ai.FP16
+        cases.append((300 + i, B, Hq, Hkv, Nq, Nk, d, dt, causal))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_prefill_cases(),
+                         ids=lambda c: f"s{c[0]}B{c[1]}Hq{c[2]}Hkv{c[3]}Nq{c[4]}Nk{c[5]}d{c[6]}{c[7]}{'c' if c[8] else 'n'}")
+def test_random_shapes(fa, case):
+    # Seeded shapes with ragged query and key tails at both head widths,
+    # GQA groups, causal with Nq <= Nk (bottom-right aligned).
+    full_case(fa, *case)
