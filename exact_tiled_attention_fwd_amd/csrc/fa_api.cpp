@@ -301,6 +301,8 @@ fa_status decode_impl(const char* fn, const void* q, const void* k_cache, const 
   if (st != FA_OK) return st;
   if (Hq / Hkv > 32) return fail(FA_ERR_UNSUPPORTED, "at most 32 q-heads per kv-head (got %d)", Hq / Hkv);
   if (B > 65535 || Hkv > 65535) return fail(FA_ERR_UNSUPPORTED, "B and Hkv must be <= 65535");
+  if ((long long)B * Hkv * (((long long)Lcap + 31) / 32) > 0x7fffffffLL)
+    return fail(FA_ERR_UNSUPPORTED, "%s: B * Hkv * ceil(Lcap / 32) must fit in int32", fn);
   size_t qb;
   if (!mul_bytes(qb, {B, Hq, d, 2})) return fail(FA_ERR_INVALID_ARG, "%s: tensor sizes overflow", fn);
   const fa::DecodePlan p = make_plan(B, Hkv, Lcap, num_splits, Hq, d);

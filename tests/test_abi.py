@@ -93,6 +93,7 @@ def dec(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(B=65535, Hq=64, Hkv=64, Lcap=1 << 20), fa.FA_ERR_UNSUPPORTED),   # block stream exceeds int32
     (dict(seqlens=None), fa.FA_ERR_INVALID_ARG),
     (dict(ws=None), fa.FA_ERR_INVALID_ARG),
     (dict(ws=FAKE + 0x4000010), fa.FA_ERR_INVALID_ARG),   # workspace not 256-aligned
