@@ -41,6 +41,23 @@ bool overlap(const void* p, size_t n, const void* q, size_t m) {
   return a < b + m && b < a + n;
 }
 
+// A byte range of one argument (ptr may be null, then it overlaps nothing).
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+// Does any output range overlap an input range or another output range?
+bool outputs_overlap(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+  for (const Span* a = outs.begin(); a != outs.end(); ++a) {
+    for (const Span& b : ins)
+      if (overlap(a->p, a->n, b.p, b.n)) return true;
+    for (const Span* b = a + 1; b != outs.end(); ++b)
+      if (overlap(a->p, a->n, b->p, b->n)) return true;
+  }
+  return false;
+}
+
 // Product of positive ints into bytes, false on overflow past 2^62.
 bool mul_bytes(size_t& out, std::initializer_list<long long> xs) {
   unsigned __int128 acc = 1;
@@ -200,9 +217,10 @@ fa_status fwd_impl(const char* fn, const void* q, const void* k, const void* v, 
     return fail(FA_ERR_UNSUPPORTED, "%s: grid too large", fn);
   const size_t qb = 2 * (size_t)(oq + 1), kb = 2 * (size_t)(ok + 1), vb = 2 * (size_t)(ov + 1),
                obb = 2 * (size_t)(oo + 1);
-  if (overlap(o, obb, q, qb) || overlap(o, obb, k, kb) || overlap(o, obb, v, vb))
+  const size_t cub = packed ? ((size_t)B + 1) * sizeof(int32_t) : 0;
+  if (outputs_overlap({{o, obb}}, {{q, qb}, {k, kb}, {v, vb}, {cu_q, cub}, {cu_k, cub}}))
     return fail(FA_ERR_INVALID_ARG, "%s: o overlaps an input", fn);
-  if (lse && (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, vb) || overlap(lse, lb, o, obb)))
+  if (lse && outputs_overlap({{lse, lb}, {o, obb}}, {{q, qb}, {k, kb}, {v, vb}, {cu_q, cub}, {cu_k, cub}}))
     return fail(FA_ERR_INVALID_ARG, "%s: lse overlaps another tensor", fn);
   st = check_device();
   if (st != FA_OK) return st;
@@ -293,7 +311,8 @@ namespace {
 fa_status decode_impl(const char* fn, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* table, const int32_t* seqlens, void* o, float* lse, void* workspace,
                       size_t workspace_bytes, int B, int Hq, int Hkv, int Lcap, int d, float scale, int num_splits,
-                      int dtype, void* stream, size_t cache_bytes, int page_size, int max_pages, int num_pages) {
+                      int dtype, void* stream, size_t cache_bytes, size_t table_bytes, int page_size, int max_pages,
+                      int num_pages) {
   if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
   if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "%s: lse must be 4-byte aligned", fn);
   if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "%s: num_splits must be >= 0", fn);
@@ -308,11 +327,10 @@ fa_status decode_impl(const char* fn, const void* q, const void* k_cache, const 
   const fa::DecodePlan p = make_plan(B, Hkv, Lcap, num_splits, Hq, d);
   if (workspace_bytes < p.ws_bytes)
     return fail(FA_ERR_INVALID_ARG, "workspace too small: %zu bytes given, %zu needed", workspace_bytes, p.ws_bytes);
-  const size_t cb = cache_bytes;
-  if (overlap(o, qb, q, qb) || overlap(o, qb, k_cache, cb) || overlap(o, qb, v_cache, cb) ||
-      overlap(workspace, p.ws_bytes, q, qb) || overlap(workspace, p.ws_bytes, k_cache, cb) ||
-      overlap(workspace, p.ws_bytes, v_cache, cb) || overlap(workspace, p.ws_bytes, o, qb))
-    return fail(FA_ERR_INVALID_ARG, "o or workspace overlaps another tensor");
+  const size_t cb = cache_bytes, lb = lse ? (size_t)B * Hq * sizeof(float) : 0, sb = (size_t)B * sizeof(int32_t);
+  if (outputs_overlap({{o, qb}, {lse, lb}, {workspace, p.ws_bytes}},
+                      {{q, qb}, {k_cache, cb}, {v_cache, cb}, {seqlens, sb}, {table, table_bytes}}))
+    return fail(FA_ERR_INVALID_ARG, "%s: o, lse or the workspace overlaps another argument", fn);
   st = check_device();
   if (st != FA_OK) return st;
   fa::DecodeArgs a{q, k_cache, v_cache, seqlens, o, lse, workspace, p.ws_lse_offset, p.ws_hdr_offset, B, Hq, Hkv,
@@ -340,7 +358,7 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, con
   size_t cb;
   if (!mul_bytes(cb, {B, Hkv, Lcap, d, 2})) return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
   return decode_impl("fa_decode", q, k_cache, v_cache, nullptr, seqlens, o, lse, workspace, workspace_bytes, B, Hq,
-                     Hkv, Lcap, d, scale, num_splits, dtype, stream, cb, 0, 0, 0);
+                     Hkv, Lcap, d, scale, num_splits, dtype, stream, cb, 0, 0, 0, 0);
 }
 
 fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,
@@ -364,8 +382,8 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
   if (!mul_bytes(cb, {num_pages, Hkv, page_size, d, 2}) || !mul_bytes(tb, {B, max_pages, 4}))
     return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
   return decode_impl("fa_decode_paged", q, k_pages, v_pages, block_table, seqlens, o, lse, workspace,
-                     workspace_bytes, B, Hq, Hkv, (int)Lcap, d, scale, num_splits, dtype, stream, cb, page_size,
-                     max_pages, num_pages);
+                     workspace_bytes, B, Hq, Hkv, (int)Lcap, d, scale, num_splits, dtype, stream, cb, tb,
+                     page_size, max_pages, num_pages);
 }
 
 fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, const float* q_descale,
@@ -397,7 +415,8 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float
   if (overlap(o, ob, q, qb) || overlap(o, ob, k, kb) || overlap(o, ob, v, kb) || overlap(o, ob, q_descale, dqb) ||
       overlap(o, ob, k_descale, dkb) || overlap(o, ob, v_descale, dkb))
     return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: o overlaps an input");
-  if (lse && (overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) || overlap(lse, lb, o, ob)))
+  if (lse && outputs_overlap({{lse, lb}, {o, ob}},
+                             {{q, qb}, {k, kb}, {v, kb}, {q_descale, dqb}, {k_descale, dkb}, {v_descale, dkb}}))
     return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: lse overlaps another tensor");
   fa_status st = check_device();
   if (st != FA_OK) return st;

@@ -112,6 +112,9 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // LDS address lds + 16 l. Written as asm so that the compiler's wait
 // insertion does not wait for these loads before every LDS read; the tile
 // loop waits for them itself before its barrier.
+// m0 carries the LDS address; it is listed as clobbered (the compiler warns
+// that m0 is reserved), and no other instruction of these kernels reads or
+// writes m0 (their assembly has no other m0 reference).
 __device__ __attribute__((always_inline)) inline void dma16(const uint16_t* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                : "memory", "m0");
@@ -390,7 +393,6 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(
     uint16_t* __restrict__ dq, int B, int Hq, int Hkv, int Nq, int Nk, float scale, float c2, int n_qt) {
   constexpr int KS = D / 16, MT = D / 32;
   constexpr int TILE = kTileRows * D * 2;
-  using ST = Stage<D>;
   __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];  // (K, V) x 2 buffers
 
   const int nbh = B * Hq;

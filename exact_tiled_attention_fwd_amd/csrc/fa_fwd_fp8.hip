@@ -88,6 +88,9 @@ __device__ inline uint32_t dma_src(int i, int w, int lane, int nvalid) {
 // LDS address lds + 16 l. Asm, so that the compiler's wait insertion, which
 // cannot tell ring slots apart, does not wait for every load in flight before
 // each LDS read; the step barriers do the waiting.
+// m0 carries the LDS address; it is listed as clobbered (the compiler warns
+// that m0 is reserved), and no other instruction of these kernels reads or
+// writes m0 (their assembly has no other m0 reference).
 __device__ __attribute__((always_inline)) inline void dma16(const uint8_t* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
                : "memory", "m0");

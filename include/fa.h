@@ -25,7 +25,10 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = legacy default stream).
  *     Work is only enqueued; the call never synchronises, allocates or frees.
  *     Results are valid once the stream has completed.
- *   - Inputs are read-only; outputs must not alias inputs.
+ *   - Inputs are read-only. Outputs and workspaces must not overlap an input
+ *     (index arrays such as seqlens and cu_seqlens included) or each other;
+ *     every call checks this on the byte ranges its arguments span and
+ *     returns FA_ERR_INVALID_ARG when they do.
  *   - Ownership: the caller allocates and frees every buffer, including the
  *     decode workspace. The library keeps only per-device properties.
  *   - Errors: every argument is validated before anything is enqueued; on

@@ -107,6 +107,11 @@ def dec(**kw):
     (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
     (dict(Hq=64, Hkv=1), fa.FA_ERR_UNSUPPORTED),          # > 32 q-heads per kv-head
     (dict(o=FAKE + 0x10), fa.FA_ERR_INVALID_ARG),         # o overlaps q
+    (dict(o=FAKE + 0x2fff800), fa.FA_ERR_INVALID_ARG),    # o runs over seqlens
+    (dict(lse=FAKE + 0x100), fa.FA_ERR_INVALID_ARG),      # lse inside q
+    (dict(lse=FAKE + 0x3100020), fa.FA_ERR_INVALID_ARG),  # lse inside o
+    (dict(lse=FAKE + 0x4000100), fa.FA_ERR_INVALID_ARG),  # lse inside the workspace
+    (dict(ws=FAKE + 0x3000000), fa.FA_ERR_INVALID_ARG),   # workspace over seqlens
 ])
 def test_decode_rejects_before_launch(kw, status):
     st = dec(**kw)
@@ -133,6 +138,8 @@ def fwd_varlen(**kw):
     (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID_ARG),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(o=FAKE + 0x100), fa.FA_ERR_INVALID_ARG),          # o overlaps q
+    (dict(o=FAKE + 0x3fff000), fa.FA_ERR_INVALID_ARG),      # o runs over cu_seqlens_q
+    (dict(lse=FAKE + 0x4100000), fa.FA_ERR_INVALID_ARG),    # lse over cu_seqlens_k
 ])
 def test_fwd_varlen_rejects_before_launch(kw, status):
     st = fwd_varlen(**kw)
@@ -275,6 +282,7 @@ def fwd_fp8(**kw):
     (dict(o=FAKE + 0x1000), fa.FA_ERR_INVALID_ARG),         # o inside q
     (dict(o=FAKE + 0x4fff00), fa.FA_ERR_INVALID_ARG),       # o over the q descales
     (dict(lse=FAKE + 0x200010), fa.FA_ERR_INVALID_ARG),     # lse inside v
+    (dict(lse=FAKE + 0x500100), fa.FA_ERR_INVALID_ARG),     # lse over the k descales
 ])
 def test_fwd_fp8_rejects_before_launch(kw, status):
     st = fwd_fp8(**kw)
@@ -301,6 +309,8 @@ def dec_paged(**kw):
     (dict(ws_bytes=16), fa.FA_ERR_INVALID_ARG),
     (dict(d=80), fa.FA_ERR_UNSUPPORTED),
     (dict(o=FAKE + 0x1000010), fa.FA_ERR_INVALID_ARG),      # o inside k_pages
+    (dict(o=FAKE + 0x27ff800), fa.FA_ERR_INVALID_ARG),      # o runs over the block table
+    (dict(lse=FAKE + 0x2800010), fa.FA_ERR_INVALID_ARG),    # lse inside the block table
 ])
 def test_decode_paged_rejects_before_launch(kw, status):
     st = dec_paged(**kw)
