@@ -178,7 +178,8 @@ fa_status fa_fwd_varlen_strided(const void* q, const void* k, const void* v, voi
  * values the 8-bit inputs stand for: element x of the (b, head) slab of q
  * stands for x * q_descale[b, head], likewise k and v with their kv-head.
  * The probabilities are rounded to FP8 for the second product (after scaling
- * by 2^8, so that they use E4M3's normal range), which bounds the accuracy:
+ * by 2^4, which keeps small values in E4M3's normal range while the running
+ * reference keeps every scaled value at most 448), which bounds the accuracy:
  * about 4% relative error on O for nearly flat attention rows; the LSE is
  * computed in fp32.
  *
