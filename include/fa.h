@@ -281,7 +281,8 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int Lcap, int d, int nu
  *            beyond rounding.
  *
  * Returns FA_OK, FA_ERR_INVALID_ARG (including a too-small workspace),
- * FA_ERR_UNSUPPORTED (also when B * Hkv * ceil(Lcap / 32) exceeds 2^31 - 1)
+ * FA_ERR_UNSUPPORTED (d, dtype or Hq / Hkv outside the ranges above, B or
+ * Hkv above 65535, or B * Hkv * ceil(Lcap / 32) above 2^31 - 1)
  * or FA_ERR_HIP.
  */
 fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
