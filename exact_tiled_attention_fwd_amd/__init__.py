@@ -58,7 +58,10 @@ _LIB = None
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "libfa.so")
+    """The library to load: ``libfa.so`` beside this file, or the build named
+    by the environment variable FA_LIBRARY (the host-sanitizer test points it
+    at ``libfa_hostsan.so``)."""
+    return os.environ.get("FA_LIBRARY") or os.path.join(_HERE, "libfa.so")
 
 
 class FAError(RuntimeError):
@@ -249,6 +252,40 @@ def _check_tensor(name, t, ndim, device=None, strided=False):
         raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} is on {t.device}, expected {device}")
 
 
+def _check_out(name, t, shape, dtype, device, strided=False):
+    """A caller-supplied output or workspace: a torch.Tensor on ``device``
+    with exactly ``shape`` and ``dtype`` (contiguous unless ``strided``, then
+    with a unit last stride). The C layer only sees a pointer, so a tensor
+    that is too small, of the wrong type or on the host must be refused
+    here, before anything is launched."""
+    if not isinstance(t, torch.Tensor):
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must be {dtype}, got {t.dtype}")
+    if strided:
+        if t.dim() and t.stride(-1) != 1 and t.shape[-1] > 1:
+            raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must have a unit stride in its last dim")
+    elif not t.is_contiguous():
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must be contiguous")
+
+
+def _check_workspace(t, need, device):
+    """A caller-supplied workspace: contiguous bytes on ``device``, at least ``need`` of them."""
+    if not isinstance(t, torch.Tensor):
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "workspace must be a torch.Tensor")
+    if t.device != device:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"workspace is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "workspace must be contiguous")
+    if t.numel() * t.element_size() < need:
+        raise FAInvalidArgument(FA_ERR_INVALID_ARG,
+                                f"workspace holds {t.numel() * t.element_size()} bytes, {need} needed")
+
+
 def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -272,12 +309,10 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, out=Non
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
-    _check_tensor("out", out, 4, dev, strided=True)
-    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
-        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "out must match q in shape and dtype")
+    _check_out("out", out, q.shape, q.dtype, dev, strided=True)
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
-    _check_tensor("lse", lse, 3, dev)
+    _check_out("lse", lse, (B, Hq, Nq), torch.float32, dev)
     with torch.cuda.device(dev):
         if all(t.is_contiguous() for t in (q, k, v, out)):
             st = fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
@@ -315,12 +350,10 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, cau
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
-    _check_tensor("out", out, 3, dev, strided=True)
-    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype:
-        raise FAInvalidArgument(FA_ERR_INVALID_ARG, "out must match q in shape and dtype")
+    _check_out("out", out, q.shape, q.dtype, dev, strided=True)
     if lse is None:
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
-    _check_tensor("lse", lse, 2, dev)
+    _check_out("lse", lse, (Hq, total_q), torch.float32, dev)
     with torch.cuda.device(dev):
         if all(t.is_contiguous() for t in (q, k, v, out)):
             st = fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
@@ -432,8 +465,8 @@ def attention_fp8(q, k, v, q_descale, k_descale, v_descale, causal: bool = False
         out = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
-    _check_tensor("out", out, 4, dev)
-    _check_tensor("lse", lse, 3, dev)
+    _check_out("out", out, (B, Hq, Nq, d), torch.bfloat16, dev)
+    _check_out("lse", lse, (B, Hq, Nq), torch.float32, dev)
     with torch.cuda.device(dev):
         st = fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(out), _ptr(lse), _ptr(q_descale), _ptr(k_descale),
                         _ptr(v_descale), B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _stream(dev))
@@ -464,12 +497,11 @@ def attention_bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | No
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for name, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
-        _check_tensor(name, t, 4, dev)
-        if tuple(t.shape) != tuple(ref.shape) or t.dtype != ref.dtype:
-            raise FAInvalidArgument(FA_ERR_INVALID_ARG, f"{name} must match the shape and dtype of its input")
+        _check_out(name, t, ref.shape, ref.dtype, dev)
     need = fa_bwd_workspace_bytes(B, Hq, Nq)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check_workspace(workspace, need, dev)
     with torch.cuda.device(dev):
         st = fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                     _ptr(workspace), workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d,
@@ -503,6 +535,9 @@ def decode(q, k_cache, v_cache, seqlens, scale: float | None = None, num_splits:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    _check_workspace(workspace, need, dev)
+    _check_out("out", out, q.shape, q.dtype, dev)
+    _check_out("lse", lse, (B, Hq), torch.float32, dev)
     with torch.cuda.device(dev):
         st = fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens), _ptr(out), _ptr(lse),
                        _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -539,6 +574,9 @@ def decode_paged(q, k_pages, v_pages, block_table, seqlens, scale: float | None 
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    _check_workspace(workspace, need, dev)
+    _check_out("out", out, q.shape, q.dtype, dev)
+    _check_out("lse", lse, (B, Hq), torch.float32, dev)
     with torch.cuda.device(dev):
         st = fa_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seqlens), _ptr(out),
                              _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(), B, Hq, Hkv,

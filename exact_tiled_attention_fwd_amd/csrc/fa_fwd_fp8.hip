@@ -165,7 +165,7 @@ __device__ __attribute__((always_inline)) inline float exp_pack8(const f32x16 (&
 
 // Online softmax step of one tile. The tile is first exponentiated against
 // the current reference m_run; every value is at most its lane's sum, so if
-// every lane's sum is at most kSumLimit the values fit E4M3 and are kept.
+// every lane's sum is at most kSumLimit8 the values fit E4M3 and are kept.
 // Otherwise (or on a row's first tile) the tile's row maximum is taken, m_run
 // moves to it, the running sum and accumulator are rescaled, and the tile is
 // exponentiated again (then every value is at most 2^kPOffset).

@@ -192,12 +192,17 @@ __device__ inline int acc_key(int r, int h) { return 8 * (r >> 2) + 4 * h + (r &
 // unite.ai, holds for any shift), so m only has to keep the exponentials in
 // range. A tile is first exponentiated against the current m with no
 // maximum taken; only when some lane's sum of those exponentials leaves
-// (0, kSumLimit] (or m is still -inf: the row's first tile) is the tile's row
+// (0, limit] (or m is still -inf: the row's first tile) is the tile's row
 // maximum taken, m moved to it, the running sum and the output accumulator
 // rescaled by exp(m_old - m_new), and the tile exponentiated again. Every p
-// is at most kSumLimit, so nothing overflows, and bf16 P keeps its relative
-// precision at any magnitude.
-constexpr float kSumLimit = 65536.f;
+// is then at most the limit, so nothing overflows and a 16-bit P keeps its
+// relative precision at any magnitude. The limit is 2^16 for bf16 and 2^15
+// for fp16, whose largest finite value (65504) is below 2^16: a P just under
+// 2^16 would round to infinity.
+template <int DT>
+constexpr float sum_limit() {
+  return DT == DT_FP16 ? 32768.f : 65536.f;
+}
 
 // One online-softmax step over NS 32-key blocks of S^T (raw scores, masked
 // entries -inf). c = scale*log2(e). Updates the row reference m_run (log2
@@ -234,7 +239,7 @@ __device__ __attribute__((always_inline)) inline void softmax_step(f32x16 (&s)[N
     ex.all();
   } else {
     psum = exp_tile<DT, NS>(s, c, m_run, pk, ex);
-    slow = __builtin_amdgcn_ballot_w64(!(psum <= kSumLimit)) != 0;
+    slow = __builtin_amdgcn_ballot_w64(!(psum <= sum_limit<DT>())) != 0;
   }
   if (slow) {
     float mx = -__builtin_inff();

@@ -346,3 +346,43 @@ def test_python_helpers_validate_tensors():
                            dropout_p=0.1)
     with pytest.raises(ValueError):            # host tensors are refused
         fa.flash_attn_func(torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64), torch.zeros(1, 4, 1, 64))
+
+
+@pytest.mark.parametrize("case,msg", [
+    ("shape", "shape"),
+    ("dtype", "float32"),
+    ("noncontig", "contiguous"),
+    ("device", "expected"),
+    ("notensor", "torch.Tensor"),
+])
+def test_caller_outputs_are_checked(case, msg):
+    """Caller-supplied out / lse tensors are refused unless they are exactly
+    what the kernel writes (the C layer only sees a pointer)."""
+    import torch
+    cpu = torch.device("cpu")
+    t, dev = torch.empty((2, 4, 8)), cpu
+    if case == "shape":
+        t = torch.empty((2, 4, 7))
+    elif case == "dtype":
+        t = torch.empty((2, 4, 8), dtype=torch.float16)
+    elif case == "noncontig":
+        t = torch.empty((2, 8, 4)).transpose(1, 2)
+    elif case == "device":
+        dev = torch.device("cuda:0")
+    elif case == "notensor":
+        t = [0.0] * 64
+    with pytest.raises(ValueError, match=msg):
+        fa._check_out("lse", t, (2, 4, 8), torch.float32, dev)
+    fa._check_out("lse", torch.empty((2, 4, 8)), (2, 4, 8), torch.float32, cpu)  # the right one passes
+
+
+def test_caller_workspace_is_checked():
+    import torch
+    cpu = torch.device("cpu")
+    with pytest.raises(ValueError, match="bytes"):
+        fa._check_workspace(torch.empty(100, dtype=torch.uint8), 101, cpu)
+    with pytest.raises(ValueError, match="expected"):
+        fa._check_workspace(torch.empty(200, dtype=torch.uint8), 101, torch.device("cuda:0"))
+    with pytest.raises(ValueError, match="contiguous"):
+        fa._check_workspace(torch.empty(40, 10, dtype=torch.uint8).t(), 101, cpu)
+    fa._check_workspace(torch.empty(26, dtype=torch.float32), 101, cpu)  # 104 bytes: enough
