@@ -7,7 +7,7 @@ PyTorch supplies device memory and the current stream.
 
 Raw entry points, same names and argument order as the C header:
     fa_fwd, fa_fwd_strided, fa_fwd_varlen, fa_fwd_varlen_strided, fa_fwd_fp8, fa_bwd,
-    fa_bwd_workspace_bytes, fa_decode, fa_decode_paged,
+    fa_bwd_workspace_bytes, fa_decode, fa_decode_noalloc, fa_decode_paged,
     fa_decode_workspace_bytes, fa_status_string, fa_last_error, fa_abi_version
 Tensor-level helpers:
     attention(q, k, v, causal=False, scale=None) -> (o, lse)
@@ -45,7 +45,7 @@ __all__ = [
     "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FAError", "lib_path", "load_library",
     "fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_varlen_strided", "fa_fwd_fp8", "attention_fp8", "fa_bwd",
     "fa_bwd_workspace_bytes",
-    "attention_bwd", "fa_decode", "fa_decode_paged",
+    "attention_bwd", "fa_decode", "fa_decode_noalloc", "fa_decode_paged",
     "fa_decode_workspace_bytes", "fa_status_string", "fa_last_error", "fa_abi_version", "attention",
     "attention_varlen", "flash_attn_func", "flash_attn_varlen_func", "decode", "decode_paged", "dtype_code",
 ]
@@ -108,6 +108,8 @@ def load_library():
     lib.fa_bwd_workspace_bytes.restype = sz
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, i, i, vp]
     lib.fa_decode.restype = i
+    lib.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp]
+    lib.fa_decode_noalloc.restype = i
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, i, i, vp]
     lib.fa_decode_paged.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i, i]
@@ -197,6 +199,14 @@ def fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, workspace_bytes,
     """Call the C ``fa_decode`` with integer device addresses; returns the status."""
     return load_library().fa_decode(q, k_cache, v_cache, seqlens, o, lse, workspace, workspace_bytes,
                                     B, Hq, Hkv, Lcap, d, scale, num_splits, dtype, stream)
+
+
+def fa_decode_noalloc(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Lcap, d, scale, num_splits, dtype,
+                      stream) -> int:
+    """Call the C ``fa_decode_noalloc`` (decode on the library's static
+    workspace) with integer device addresses; returns the status."""
+    return load_library().fa_decode_noalloc(q, k_cache, v_cache, seqlens, o, lse, B, Hq, Hkv, Lcap, d, scale,
+                                            num_splits, dtype, stream)
 
 
 def fa_decode_paged(q, k_pages, v_pages, block_table, seqlens, o, lse, workspace, workspace_bytes,

@@ -18,6 +18,8 @@
 #include "fa_fp8_launch.h"
 #include "fa_launch.h"
 
+static_assert(fa::kNoAllocScratchBytes == FA_NOALLOC_SCRATCH_BYTES, "static decode workspace size");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -359,6 +361,36 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, con
   if (!mul_bytes(cb, {B, Hkv, Lcap, d, 2})) return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
   return decode_impl("fa_decode", q, k_cache, v_cache, nullptr, seqlens, o, lse, workspace, workspace_bytes, B, Hq,
                      Hkv, Lcap, d, scale, num_splits, dtype, stream, cb, 0, 0, 0, 0);
+}
+
+fa_status fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
+                            void* o, float* lse, int B, int Hq, int Hkv, int Lcap, int d, float scale, int num_splits,
+                            int dtype, void* stream) {
+  g_last_error.clear();
+  if (!q || !k_cache || !v_cache || !seqlens || !o)
+    return fail(FA_ERR_INVALID_ARG, "q, k_cache, v_cache, seqlens and o must be non-null");
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16))
+    return fail(FA_ERR_INVALID_ARG, "q, k_cache, v_cache and o must be 16-byte aligned");
+  if (!aligned(seqlens, 4)) return fail(FA_ERR_INVALID_ARG, "seqlens must be 4-byte aligned");
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Lcap <= 0 || d <= 0)
+    return fail(FA_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d Lcap=%d d=%d)", B, Hq, Hkv, Lcap, d);
+  if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "fa_decode_noalloc: num_splits must be >= 0");
+  fa_status st = check_common(d, dtype, scale, Hq, Hkv);
+  if (st != FA_OK) return st;
+  size_t cb;
+  if (!mul_bytes(cb, {B, Hkv, Lcap, d, 2})) return fail(FA_ERR_INVALID_ARG, "tensor sizes overflow");
+  const size_t need = make_plan(B, Hkv, Lcap, num_splits, Hq, d).ws_bytes;
+  if (need > fa::kNoAllocScratchBytes)
+    return fail(FA_ERR_INVALID_ARG,
+                "fa_decode_noalloc: this decode needs a %zu-byte workspace, more than the %zu-byte static one "
+                "(use fa_decode with a caller-owned workspace)", need, fa::kNoAllocScratchBytes);
+  st = check_device();
+  if (st != FA_OK) return st;
+  void* ws = nullptr;
+  const hipError_t e = fa::noalloc_scratch(&ws);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "fa_decode_noalloc: scratch address: %s", hipGetErrorString(e));
+  return decode_impl("fa_decode_noalloc", q, k_cache, v_cache, nullptr, seqlens, o, lse, ws, fa::kNoAllocScratchBytes,
+                     B, Hq, Hkv, Lcap, d, scale, num_splits, dtype, stream, cb, 0, 0, 0, 0);
 }
 
 fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, const int32_t* block_table,

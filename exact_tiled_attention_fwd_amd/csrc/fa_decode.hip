@@ -460,6 +460,32 @@ hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// Workspace of fa_decode_noalloc: a file-scope device array, one copy per
+// GPU, held for the life of the process. Host code never passes the array's
+// name to a kernel (on the host it only stands for the symbol): its device
+// address is looked up once per device with hipGetSymbolAddress, with that
+// device current, and cached.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 256;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.dtype == DT_BF16) return a.d == 128 ? launch_decode_t<DT_BF16, 128>(a, stream) : launch_decode_t<DT_BF16, 64>(a, stream);
   return a.d == 128 ? launch_decode_t<DT_FP16, 128>(a, stream) : launch_decode_t<DT_FP16, 64>(a, stream);

@@ -72,4 +72,10 @@ constexpr int kFwdBlockRows = 256;  // query rows per prefill workgroup
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// The static decode workspace behind fa_decode_noalloc (fa.h): its size and
+// its device address on the current device (looked up on the first call
+// per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace fa

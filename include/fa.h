@@ -291,6 +291,29 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, con
                     int dtype, void* stream);
 
 /*
+ * fa_decode_noalloc - fa_decode without a caller-supplied workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.
+ *
+ * Arguments, layouts, results and errors are those of fa_decode without
+ * `workspace` and `workspace_bytes`. The workspace is a static device array
+ * of FA_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library, one per GPU,
+ * held until the process ends; its address is looked up on the first call
+ * on each device (with that device current). The call allocates nothing
+ * and frees nothing. Sizes whose fa_decode_workspace_bytes(...) exceeds the
+ * array are refused with FA_ERR_INVALID_ARG before anything is launched.
+ *
+ * Every call on one GPU uses the same array and the last call's contents
+ * stay in it (nothing in it needs to start at zero): calls that overlap on
+ * one GPU (different streams, or threads, without ordering between them)
+ * race. Order them on one stream, or use fa_decode with separate workspaces.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+fa_status fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seqlens,
+                            void* o, float* lse, int B, int Hq, int Hkv, int Lcap, int d, float scale,
+                            int num_splits, int dtype, void* stream);
+
+/*
  * fa_decode_paged - fa_decode with the KV cache held in fixed-size pages
  * reached through a per-sequence page table.
  *

@@ -386,3 +386,19 @@ def test_caller_workspace_is_checked():
     with pytest.raises(ValueError, match="contiguous"):
         fa._check_workspace(torch.empty(40, 10, dtype=torch.uint8).t(), 101, cpu)
     fa._check_workspace(torch.empty(26, dtype=torch.float32), 101, cpu)  # 104 bytes: enough
+
+
+def test_decode_noalloc_rejects_before_launch():
+    """The static-workspace decode validates like fa_decode, and refuses
+    sizes whose workspace exceeds the static array, before any HIP call."""
+    base = dict(q=FAKE, k_cache=FAKE, v_cache=FAKE, seqlens=FAKE, o=FAKE * 2, lse=None, B=2, Hq=8, Hkv=2, Lcap=512,
+                d=128, scale=0.1, num_splits=0, dtype=fa.FA_DTYPE_BF16, stream=None)
+    for kw, status in ((dict(q=None), fa.FA_ERR_INVALID_ARG), (dict(o=FAKE + 4), fa.FA_ERR_INVALID_ARG),
+                       (dict(d=96), fa.FA_ERR_UNSUPPORTED), (dict(Hq=7), fa.FA_ERR_INVALID_ARG),
+                       (dict(num_splits=-1), fa.FA_ERR_INVALID_ARG), (dict(scale=0.0), fa.FA_ERR_INVALID_ARG)):
+        assert fa.fa_decode_noalloc(**{**base, **kw}) == status, kw
+    # 64 sequences x 32 q-heads at Lcap 32768: a 68 MB workspace, above the 64 MiB array
+    big = dict(base, B=64, Hq=32, Hkv=8, Lcap=32768)
+    assert fa.fa_decode_workspace_bytes(64, 32, 8, 32768, 128, 0) > (64 << 20)
+    assert fa.fa_decode_noalloc(**big) == fa.FA_ERR_INVALID_ARG
+    assert "static" in fa.fa_last_error()
