@@ -1,26 +1,31 @@
-"""The block-by-block softmax of FlashAttention, in float64 (TEST INFRASTRUCTURE).
+"""Attention from block-wise partial softmaxes and the merge identity, in
+float64 (TEST INFRASTRUCTURE).
 
 Source: "Flash Attention: Revolutionizing Transformer Efficiency" (unite.ai),
-sections "The math of Flash Attention" (softmax decomposition and the merge of
-two partial softmaxes) and "Implementation details" (an outer loop over query
-blocks, an inner loop over key/value blocks, running row maximum M and running
-sum L).
+section "The math of Flash Attention": the softmax over the union of two sets
+of scores follows from the softmaxes of the parts, each rescaled by the
+exponential of its own maximum minus the maximum of the union; section
+"Flash Attention algorithm": the scores are taken block by block and never
+held whole.
 
-Reading of the merge identity: the page's printed merge wraps the rescaled
-partial results in a second softmax, which is not what its own loop does. The
-plainest reading that the loop supports: keep the unnormalised partial
-f(x) = exp(x - m_x) with l(x) = sum f(x); for two parts with m = max(m_x, m_y),
-f(x u y) is the concatenation of exp(m_x - m) f(x) and exp(m_y - m) f(y), and
-l(x u y) = exp(m_x - m) l(x) + exp(m_y - m) l(y).
+Reading of the merge identity: the page prints the merge wrapped in a second
+softmax, which its own code does not do. The plainest reading the rest of the
+page supports keeps unnormalised partials. For a set x of scores of one row,
+m(x) = max x, f(x) = exp(x - m(x)), l(x) = sum f(x) and acc(x) = f(x) V(x).
+For disjoint x and y with m = max(m(x), m(y)):
+    l(x u y)   = exp(m(x) - m) l(x)   + exp(m(y) - m) l(y)
+    acc(x u y) = exp(m(x) - m) acc(x) + exp(m(y) - m) acc(y)
+and the result is O = acc / l, LSE = m + log l. (The FlashAttention-2 form
+of the output update, with the division by l deferred to the end.)
 
-Reading of the output update: the page's loop multiplies the already
-normalised output by the rescale factor alone and divides by the new sum, which
-is wrong as soon as a row spans more than one key block. The reading used here
-keeps the unnormalised accumulator acc = alpha * acc + P V and divides by l once
-after the last block (the deferred normalisation of FlashAttention-2).
+Here each (query block, key block) partial is computed on its own and the
+partials of a query block are folded pairwise as a balanced tree (adjacent
+pairs first), so the identity is pinned for partials of any sizes in any
+grouping, not only as a running update. ``merge_partials`` is the same
+identity for normalised parts in LSE form (used by the split-key decode).
 
-This module exists to pin the identity against the one-shot definition in
-``attention.py``; it is test infrastructure.
+This module pins the identity against the one-shot definition in
+``exact.py``; it is test infrastructure.
 """
 from __future__ import annotations
 
@@ -29,8 +34,41 @@ import numpy as np
 from .exact import as_fp32_scale
 
 
+def block_partial(q, k, v, sigma, rows, cols, Nk_minus_Nq, causal):
+    """(m, l, acc) of one query block against one key block.
+
+    rows / cols are the absolute query / key indices of the blocks; a key
+    is visible to a query iff causal is off or col <= row + (Nk - Nq). Rows
+    with no visible key get m = -inf, l = 0, acc = 0."""
+    s = sigma * (q @ k.T)
+    vis = (cols[None, :] <= rows[:, None] + Nk_minus_Nq) if causal else np.ones_like(s, bool)
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1) if s.shape[1] else np.full(s.shape[0], -np.inf)
+    ref = np.where(np.isfinite(m), m, 0.0)
+    f = np.where(vis, np.exp(s - ref[:, None]), 0.0)
+    return m, f.sum(axis=1), f @ v
+
+
+def merge_two(a, b):
+    """The merge identity for two unnormalised partials over disjoint keys."""
+    (ma, la, acca), (mb, lb, accb) = a, b
+    m = np.maximum(ma, mb)
+    ref = np.where(np.isfinite(m), m, 0.0)
+    wa = np.where(np.isfinite(ma), np.exp(ma - ref), 0.0)
+    wb = np.where(np.isfinite(mb), np.exp(mb - ref), 0.0)
+    return m, wa * la + wb * lb, wa[:, None] * acca + wb[:, None] * accb
+
+
+def fold(parts):
+    """Merge a list of partials as a balanced tree of adjacent pairs."""
+    while len(parts) > 1:
+        parts = [merge_two(parts[i], parts[i + 1]) if i + 1 < len(parts) else parts[i]
+                 for i in range(0, len(parts), 2)]
+    return parts[0]
+
+
 def blockwise_attention_head(q, k, v, scale, causal=False, block_q=64, block_k=64):
-    """Tiled attention for one head with running (m, l, acc); float64 throughout."""
+    """One head from block partials merged by the identity; float64 throughout."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -41,26 +79,16 @@ def blockwise_attention_head(q, k, v, scale, causal=False, block_q=64, block_k=6
     for i0 in range(0, Nq, block_q):
         qi = q[i0:i0 + block_q]
         rows = np.arange(i0, i0 + qi.shape[0])
-        m = np.full(qi.shape[0], -np.inf)
-        l = np.zeros(qi.shape[0])
-        acc = np.zeros((qi.shape[0], v.shape[1]))
-        for j0 in range(0, Nk, block_k):
-            kj, vj = k[j0:j0 + block_k], v[j0:j0 + block_k]
-            s = sigma * (qi @ kj.T)
-            cols = np.arange(j0, j0 + kj.shape[0])
-            vis = (cols[None, :] <= rows[:, None] + (Nk - Nq)) if causal else np.ones_like(s, bool)
-            s = np.where(vis, s, -np.inf)
-            m_new = np.maximum(m, s.max(axis=1))
-            ref = np.where(np.isfinite(m_new), m_new, 0.0)  # nothing visible yet: keep zeros
-            alpha = np.exp(m - ref)
-            p = np.where(vis, np.exp(s - ref[:, None]), 0.0)
-            l = alpha * l + p.sum(axis=1)
-            acc = alpha[:, None] * acc + p @ vj
-            m = m_new
+        parts = [block_partial(qi, k[j0:j0 + block_k], v[j0:j0 + block_k], sigma, rows,
+                               np.arange(j0, min(j0 + block_k, Nk)), Nk - Nq, causal)
+                 for j0 in range(0, Nk, block_k)]
+        if not parts:
+            continue
+        m, l, acc = fold(parts)
         ok = l > 0
-        O[i0:i0 + qi.shape[0]] = np.where(ok[:, None], acc / np.where(ok, l, 1.0)[:, None], 0.0)
+        O[rows] = np.where(ok[:, None], acc / np.where(ok, l, 1.0)[:, None], 0.0)
         with np.errstate(divide="ignore"):
-            LSE[i0:i0 + qi.shape[0]] = np.where(ok, m + np.log(np.where(ok, l, 1.0)), -np.inf)
+            LSE[rows] = np.where(ok, m + np.log(np.where(ok, l, 1.0)), -np.inf)
     return O, LSE
 
 
