@@ -204,11 +204,11 @@ constexpr float sum_limit() {
   return DT == DT_FP16 ? 32768.f : 65536.f;
 }
 
-// One online-softmax step over NS 32-key blocks of S^T (raw scores, masked
-// entries -inf). c = scale*log2(e). Updates the row reference m_run (log2
-// units, per lane = per query column), this lane's share of the running sum
-// l_run, rescales acc_o when m_run moves, and returns P rounded to the input
-// type, packed two per register in accumulator order.
+// Exponentiates NS 32-key blocks of S^T (raw scores, masked entries -inf)
+// against the reference m_use (log2 units): P = exp2(c s - m_use) with
+// c = scale*log2(e), rounded to the input type and packed two per register
+// in accumulator order into pk. Returns this lane's sum of the unrounded P.
+// ex(i) is called once per pair of exponentials (i = 0 .. 8 NS - 1).
 template <int DT, int NS, class EX = NoExtra>
 __device__ __attribute__((always_inline)) inline float exp_tile(const f32x16 (&s)[NS], float c, float m_use,
                                                                  uint32_t (&pk)[NS][8], const EX& ex = EX{}) {
@@ -226,9 +226,36 @@ __device__ __attribute__((always_inline)) inline float exp_tile(const f32x16 (&s
   return psum;
 }
 
-// ex(i) is called once per pair of exponentials (i = 0 .. 8 NS - 1) of the
-// pass against the current reference point; a row's first tile, which has
-// no such pass, calls ex.all() instead.
+// The slow branch of the rule: take the tile's row maximum, move the
+// reference to it, rescale the running sum and the accumulator by
+// exp2(m_old - m_new), and exponentiate the tile again. Returns the new sum.
+template <int DT, int NS, int MT>
+__device__ __attribute__((always_inline)) inline float move_reference(const f32x16 (&s)[NS], float c, float& m_run,
+                                                                      float& l_run, f32x16 (&acc_o)[MT],
+                                                                      uint32_t (&pk)[NS][8]) {
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int kb = 0; kb < NS; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  mx = halves_max(mx) * c;
+  const float m_new = fmaxf(m_run, mx);
+  const float alpha = (m_new == -__builtin_inff()) ? 1.f : exp2_fast(m_run - m_new);
+  l_run *= alpha;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
+  m_run = m_new;
+  return exp_tile<DT, NS>(s, c, (m_new == -__builtin_inff()) ? 0.f : m_new, pk);
+}
+
+// One online-softmax step over NS 32-key blocks of S^T. Updates the row
+// reference m_run (per lane = per query column), this lane's share of the
+// running sum l_run, rescales acc_o when m_run moves, and leaves P in pk.
+// ex(i) is called once per pair of exponentials of the pass against the
+// current reference point; a row's first tile, which has no such pass,
+// calls ex.all() instead.
 template <int DT, int NS, int MT, class EX = NoExtra>
 __device__ __attribute__((always_inline)) inline void softmax_step(f32x16 (&s)[NS], float c, float& m_run,
                                                                    float& l_run, f32x16 (&acc_o)[MT],
@@ -241,23 +268,7 @@ __device__ __attribute__((always_inline)) inline void softmax_step(f32x16 (&s)[N
     psum = exp_tile<DT, NS>(s, c, m_run, pk, ex);
     slow = __builtin_amdgcn_ballot_w64(!(psum <= sum_limit<DT>())) != 0;
   }
-  if (slow) {
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int kb = 0; kb < NS; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = halves_max(mx) * c;
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_new == -__builtin_inff()) ? 1.f : exp2_fast(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[mt][r] *= alpha;
-    m_run = m_new;
-    psum = exp_tile<DT, NS>(s, c, (m_new == -__builtin_inff()) ? 0.f : m_new, pk);
-  }
+  if (slow) psum = move_reference<DT, NS, MT>(s, c, m_run, l_run, acc_o, pk);
   l_run += psum;
 }
 
