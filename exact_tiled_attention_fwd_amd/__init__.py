@@ -8,7 +8,8 @@ PyTorch supplies device memory and the current stream.
 Raw entry points, same names and argument order as the C header:
     fa_fwd, fa_fwd_strided, fa_fwd_varlen, fa_fwd_varlen_strided, fa_fwd_fp8, fa_bwd,
     fa_bwd_workspace_bytes, fa_decode, fa_decode_noalloc, fa_decode_paged,
-    fa_decode_workspace_bytes, fa_status_string, fa_last_error, fa_abi_version
+    fa_decode_workspace_bytes, fa_set_prefill_schedule, fa_status_string, fa_last_error,
+    fa_abi_version
 Tensor-level helpers:
     attention(q, k, v, causal=False, scale=None) -> (o, lse)
         q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d], any strides with a unit last one
@@ -42,7 +43,8 @@ import torch  # loads the HIP runtime that libfa.so then binds to
 
 __all__ = [
     "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_HIP",
-    "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FAError", "lib_path", "load_library",
+    "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FA_SCHEDULE_AUTO", "FA_SCHEDULE_TILES", "FA_SCHEDULE_SPLIT",
+    "FAError", "lib_path", "load_library", "fa_set_prefill_schedule",
     "fa_fwd", "fa_fwd_strided", "fa_fwd_varlen", "fa_fwd_varlen_strided", "fa_fwd_fp8", "attention_fp8", "fa_bwd",
     "fa_bwd_workspace_bytes",
     "attention_bwd", "fa_decode", "fa_decode_noalloc", "fa_decode_paged",
@@ -52,6 +54,7 @@ __all__ = [
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 FA_DTYPE_BF16, FA_DTYPE_FP16 = 0, 1
+FA_SCHEDULE_AUTO, FA_SCHEDULE_TILES, FA_SCHEDULE_SPLIT = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -120,6 +123,8 @@ def load_library():
     lib.fa_last_error.restype = ctypes.c_char_p
     lib.fa_abi_version.argtypes = []
     lib.fa_abi_version.restype = i
+    lib.fa_set_prefill_schedule.argtypes = [i]
+    lib.fa_set_prefill_schedule.restype = i
     _LIB = lib
     return lib
 
@@ -137,6 +142,12 @@ def _raise_for(status: int):
 
 
 # ------------------------------------------------------------------ raw C ABI
+def fa_set_prefill_schedule(mode: int) -> int:
+    """Call the C ``fa_set_prefill_schedule`` (FA_SCHEDULE_*); returns the
+    previous mode, or -1 for an unknown one."""
+    return load_library().fa_set_prefill_schedule(mode)
+
+
 def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, stream) -> int:
     """Call the C ``fa_fwd`` with integer device addresses; returns the status."""
     return load_library().fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, stream)

@@ -251,6 +251,8 @@ const char* fa_status_string(int s) {
 
 const char* fa_last_error(void) { return g_last_error.c_str(); }
 
+int fa_set_prefill_schedule(int mode) { return fa::set_fwd_schedule(mode); }
+
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
                  int Nk, int d, float scale, int causal, int dtype, void* stream) {
   g_last_error.clear();

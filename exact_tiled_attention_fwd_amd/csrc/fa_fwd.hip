@@ -15,6 +15,9 @@
 // and is read transposed (ds_read_b64_tr_b16) as the A operand of
 // O^T += V^T P^T, so no lane shuffles are needed anywhere. The vector ALUs are
 // left to the softmax.
+#include <atomic>
+
+#include "fa.h"
 #include "fa_launch.h"
 #include "fa_tile.h"
 
@@ -27,6 +30,7 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kBM = kFwdBlockRows;  // 256 query rows per workgroup
+constexpr int kBMs = 128;           // query rows per item in split mode
 constexpr int kThreads = 512;       // 8 waves = 2 groups of 4
 constexpr int kSlots = 4;           // ring depth for K and for V
 
@@ -131,9 +135,11 @@ struct DmaReader {
   }
 };
 
-// The 8 tile loads of one step, slotted in after MFMAs 2, 6, ..., 30 of a
-// 32-op matrix-core phase, so that the loads of the four loading waves reach
-// the address unit a few at a time instead of in one burst. Full tiles only.
+// The 8 tile loads of one step, slotted in after every (N / 8)-th MFMA of an
+// N-op matrix-core phase (MFMAs 2, 6, ..., 30 of 32; 1, 3, ..., 15 of 16), so
+// that the loads of the four loading waves reach the address unit a few at a
+// time instead of in one burst. Full tiles only.
+template <int N>
 struct DmaSpread {
   const uint16_t* kbase;
   const uint16_t* vbase;
@@ -142,8 +148,10 @@ struct DmaSpread {
   uint32_t dk, dv;
   long long kstep, vstep;  // RPI rows, in elements
   __device__ __attribute__((always_inline)) void operator()(int t) const {
-    if ((t & 3) != 2) return;
-    const int j = t >> 2;
+    constexpr int ST = N / 8;
+    static_assert(ST * 8 == N, "phase length");
+    if (t % ST != ST / 2) return;
+    const int j = t / ST;
     if (j < 4) {
       if (has_k) dma16(kbase + kstep * j, dk, kslot + 4096 * j);
     } else {
@@ -152,13 +160,21 @@ struct DmaSpread {
   }
 };
 
-template <int DT, int D, bool CAUSAL, bool VARLEN>
+// Split mode (causal grids too small to fill the GPU): a workgroup takes the
+// 128-row blocks nb - 1 - qt and qt of one head in turn, so every workgroup
+// has the same number of visible keys. Waves w and w + 4 hold the same 32
+// query rows and the two groups take the two halves of every key tile; at
+// the end of a block the halves are joined by the merge identity of "The
+// math of Flash Attention" through LDS. Tiles, ring and loads are those of
+// the 256-row mode.
+template <int DT, int D, bool CAUSAL, bool VARLEN, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Nq_all, int Nk_all,
     float scale_log2, int n_qt, Varlen vlen, Layout ly) {
   constexpr int ROWS = Geo<D>::ROWS, kTile = Geo<D>::TILE, RPI = Geo<D>::RPI;
-  constexpr int KS = D / 16, KB = ROWS / 32, MT = D / 32;
+  constexpr int WR = SPLIT ? ROWS / 2 : ROWS;  // keys of a tile one wave multiplies
+  constexpr int KS = D / 16, KB = WR / 32, MT = D / 32;
   using Rd = DmaReader<D>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * kSlots * kTile];
   char* const kring = smem;                   // K tile t in slot t % 4
@@ -167,13 +183,18 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
   const Work wk = VARLEN ? map_work_packed(blockIdx.x, B, Hq, Hkv, n_qt) : map_work(blockIdx.x, B, Hq, Hkv, n_qt);
   const Slabs sl = slabs_of<VARLEN>(wk, q, k, v, o, lse, Hq, Nq_all, Nk_all, vlen, ly);
   const int Nq = sl.Nq, Nk = sl.Nk;
-  const int q0 = wk.qt * kBM;
+  const int nb = (Nq + kBMs - 1) / kBMs;
+  const int n_items = SPLIT && nb - 1 - wk.qt > wk.qt ? 2 : 1;
+  for (int item = 0; item < n_items; ++item) {
+  const int q0 = SPLIT ? kBMs * (item == 0 ? nb - 1 - wk.qt : wk.qt) : wk.qt * kBM;
   if (VARLEN && q0 >= Nq) return;  // past this sequence's rows (the whole workgroup)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int grp = wave >> 2;  // 0: matrix cores first; 1: softmax first
-  const int q0w = q0 + 32 * wave;  // first query row of this wave
+  const int q0w = q0 + 32 * (SPLIT ? (wave & 3) : wave);  // first query row of this wave
   const int off = Nk - Nq;         // causal: key j visible to query i iff j <= i + off
+  const int key0 = SPLIT ? grp * WR : 0;            // first key of a tile this wave multiplies
+  const uint32_t koff = (uint32_t)(key0 * 2 * D);  // its byte offset in a ring slot
 
   const uint16_t* qp = sl.q;
   const uint16_t* kp = sl.k;
@@ -182,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
   // Key tiles this workgroup visits (none for rows that see no key).
   int n_kv = (Nk + ROWS - 1) / ROWS;
   if (CAUSAL) {
-    const int last_key = min(q0 + kBM, Nq) - 1 + off;
+    const int last_key = min(q0 + (SPLIT ? kBMs : kBM), Nq) - 1 + off;
     n_kv = last_key < 0 ? 0 : min(n_kv, last_key / ROWS + 1);
   }
   // Key tiles this wave computes on (0 if the wave has no valid query row).
@@ -190,7 +211,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
   int wave_tiles = wave_active ? n_kv : 0;
   if (CAUSAL && wave_active) {
     const int last = min(q0w + 31, Nq - 1) + off;
-    wave_tiles = last < 0 ? 0 : min(n_kv, last / ROWS + 1);
+    wave_tiles = last < key0 ? 0 : min(n_kv, (last - key0) / ROWS + 1);
   }
 
   // Q^T operand (B operand of S^T = K Q^T), held for the whole loop.
@@ -219,8 +240,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
 
   // SM(j): mask the ragged key tail / causal diagonal, online softmax -> pk.
   auto softmax = [&](int j) {
-    const int j0 = j * ROWS;
-    const bool need_mask = (j0 + ROWS > Nk) || (CAUSAL && j0 + ROWS - 1 > q0w + off);
+    const int j0 = j * ROWS + key0;
+    const bool need_mask = (j0 + WR > Nk) || (CAUSAL && j0 + WR - 1 > q0w + off);
     if (need_mask) {
       const int lim = CAUSAL ? min(Nk, qrow + off + 1) : Nk;  // keys < lim are visible
 #pragma unroll
@@ -235,24 +256,24 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
   // mma_pre issues the first operand reads; mma finishes the phase.
   u32x4 obuf[kPF];
   auto mma_pre = [&](bool do_o, int jo, bool do_s, int js) {
-    const char* vl = vring + (jo % kSlots) * kTile;
-    const char* kl = kring + (js % kSlots) * kTile;
+    const char* vl = vring + (jo % kSlots) * kTile + koff;
+    const char* kl = kring + (js % kSlots) * kTile + koff;
     if (do_o && do_s)
-      mma_prefetch<D, ROWS, true, true, Rd>(obuf, vl, kl, lane);
+      mma_prefetch<D, WR, true, true, Rd>(obuf, vl, kl, lane);
     else if (do_o)
-      mma_prefetch<D, ROWS, true, false, Rd>(obuf, vl, kl, lane);
+      mma_prefetch<D, WR, true, false, Rd>(obuf, vl, kl, lane);
     else if (do_s)
-      mma_prefetch<D, ROWS, false, true, Rd>(obuf, vl, kl, lane);
+      mma_prefetch<D, WR, false, true, Rd>(obuf, vl, kl, lane);
   };
   auto mma = [&](bool do_o, int jo, bool do_s, int js) {
-    const char* vl = vring + (jo % kSlots) * kTile;
-    const char* kl = kring + (js % kSlots) * kTile;
+    const char* vl = vring + (jo % kSlots) * kTile + koff;
+    const char* kl = kring + (js % kSlots) * kTile + koff;
     if (do_o && do_s)
-      mma_run<DT, D, ROWS, true, true, Rd>(obuf, vl, kl, pk, qop, acc_o, s, lane);
+      mma_run<DT, D, WR, true, true, Rd>(obuf, vl, kl, pk, qop, acc_o, s, lane);
     else if (do_o)
-      mma_run<DT, D, ROWS, true, false, Rd>(obuf, vl, kl, pk, qop, acc_o, s, lane);
+      mma_run<DT, D, WR, true, false, Rd>(obuf, vl, kl, pk, qop, acc_o, s, lane);
     else if (do_s)
-      mma_run<DT, D, ROWS, false, true, Rd>(obuf, vl, kl, pk, qop, acc_o, s, lane);
+      mma_run<DT, D, WR, false, true, Rd>(obuf, vl, kl, pk, qop, acc_o, s, lane);
   };
 
   // ---- direct-to-LDS tile loads, issued by the waves of group 0 only (they
@@ -317,20 +338,20 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
         // full phase: with full tiles the loads are spread over its MFMAs
         const bool spread = (!has_k || Nk - (i + 2) * ROWS >= ROWS) && (!has_v || Nk - (i + 1) * ROWS >= ROWS);
         if (!spread) issue_step(i);
-        const DmaSpread ex{kp + (long long)(i + 2) * ROWS * sl.ks, vp + (long long)(i + 1) * ROWS * sl.vs,
+        const DmaSpread<MmaPlan<D, WR, true, true, Rd>::N> ex{kp + (long long)(i + 2) * ROWS * sl.ks, vp + (long long)(i + 1) * ROWS * sl.vs,
                            lds_k + (uint32_t)(((i + 2) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
                            lds_v + (uint32_t)(((i + 1) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
                            has_k && spread, has_v && spread, dk, dv, kstep, vstep};
-        mma_run<DT, D, ROWS, true, true, Rd>(obuf, vring + ((i - 1) % kSlots) * kTile,
-                                                    kring + (i % kSlots) * kTile, pk, qop, acc_o, s, lane, ex);
+        mma_run<DT, D, WR, true, true, Rd>(obuf, vring + ((i - 1) % kSlots) * kTile + koff,
+                                                  kring + (i % kSlots) * kTile + koff, pk, qop, acc_o, s, lane, ex);
       } else {
         issue_step(i);
         if (do_o)
-          mma_run<DT, D, ROWS, true, false, Rd>(obuf, vring + ((i - 1) % kSlots) * kTile,
-                                                       kring + (i % kSlots) * kTile, pk, qop, acc_o, s, lane);
+          mma_run<DT, D, WR, true, false, Rd>(obuf, vring + ((i - 1) % kSlots) * kTile + koff,
+                                                     kring + (i % kSlots) * kTile + koff, pk, qop, acc_o, s, lane);
         else if (do_s)
-          mma_run<DT, D, ROWS, false, true, Rd>(obuf, vring, kring + (i % kSlots) * kTile, pk, qop, acc_o,
-                                                       s, lane);
+          mma_run<DT, D, WR, false, true, Rd>(obuf, vring + koff, kring + (i % kSlots) * kTile + koff, pk, qop,
+                                                     acc_o, s, lane);
       }
       dma_barrier(n_new);  // Y_i
       if (i < wave_tiles) softmax(i);
@@ -346,24 +367,87 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
     }
   }
 
-  if (!wave_active) return;
   // ---- epilogue: normalise once, write O and LSE
-  const float l_tot = halves_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qrow < Nq) {
-    uint16_t* orow = sl.o + (size_t)qrow * sl.os;
+  auto epilogue = [&]() {
+    const float l_tot = halves_sum(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow < Nq) {
+      uint16_t* orow = sl.o + (size_t)qrow * sl.os;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d0 = 32 * mt + 8 * i + 4 * half;
-        const u32x2 w = {pack2<DT>(acc_o[mt][4 * i] * inv, acc_o[mt][4 * i + 1] * inv),
-                         pack2<DT>(acc_o[mt][4 * i + 2] * inv, acc_o[mt][4 * i + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d0) = w;
-      }
-    if (sl.lse != nullptr && half == 0)
-      sl.lse[qrow] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
+        for (int i = 0; i < 4; ++i) {
+          const int d0 = 32 * mt + 8 * i + 4 * half;
+          const u32x2 w = {pack2<DT>(acc_o[mt][4 * i] * inv, acc_o[mt][4 * i + 1] * inv),
+                           pack2<DT>(acc_o[mt][4 * i + 2] * inv, acc_o[mt][4 * i + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d0) = w;
+        }
+      if (sl.lse != nullptr && half == 0)
+        sl.lse[qrow] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
+    }
+  };
+  if constexpr (!SPLIT) {
+    if (!wave_active) return;
+    epilogue();
+  } else {
+    // Join the two key halves of each row. Group 1 leaves its (m, l, O^T
+    // accumulator) in LDS, in the ring whose last reads the first barrier
+    // orders; group 0 merges them into its own and writes the block. The
+    // third barrier keeps the next block's loads off the buffer until then.
+    constexpr int XW = 16 * MT + 2;  // floats per lane
+    float* const xb = reinterpret_cast<float*>(smem) + (wave & 3) * (XW * 64) + lane;
+    __syncthreads();
+    if (grp == 1) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xb[(16 * mt + r) * 64] = acc_o[mt][r];
+      xb[16 * MT * 64] = m_run;
+      xb[(16 * MT + 1) * 64] = l_run;
+    }
+    __syncthreads();
+    if (grp == 0) {
+      const float m1 = xb[16 * MT * 64], l1 = xb[(16 * MT + 1) * 64];
+      const float m = fmaxf(m_run, m1);
+      const float a0 = m_run == -__builtin_inff() ? 0.f : exp2_fast(m_run - m);
+      const float a1 = m1 == -__builtin_inff() ? 0.f : exp2_fast(m1 - m);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[mt][r] = a0 * acc_o[mt][r] + a1 * xb[(16 * mt + r) * 64];
+      l_run = a0 * l_run + a1 * l1;
+      m_run = m;
+      if (wave_active) epilogue();
+    }
+    __syncthreads();
   }
+  }  // item
+}
+
+// Compute units of the current device (0 if the query fails), asked once per device.
+int device_cus() {
+  static std::atomic<int> cache[256];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return 0;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
+std::atomic<int> g_schedule{FA_SCHEDULE_AUTO};
+
+// Split mode when a causal grid of 256-row workgroups fits on the GPU at
+// once: the workgroup of the last query tile then sets the time, while in
+// split mode every workgroup has the same work. A grid of several rounds is
+// balanced already by the heaviest-first order.
+bool use_split(long long nblocks, int rows) {
+  const int mode = g_schedule.load(std::memory_order_relaxed);
+  if (mode != FA_SCHEDULE_AUTO) return mode == FA_SCHEDULE_SPLIT;
+  const int cus = device_cus();
+  return rows > kBMs && cus > 0 && nblocks <= cus;
 }
 
 template <int DT, int D, bool CAUSAL, bool VARLEN>
@@ -374,8 +458,18 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (nblocks == 0) return hipSuccess;
   const Varlen vl{a.cu_q, a.cu_k, a.total_q, a.total_k};
-  hipLaunchKernelGGL((fa_fwd_kernel<DT, D, CAUSAL, VARLEN>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
+  if constexpr (CAUSAL && !VARLEN) {
+    if (use_split(nblocks, rows)) {
+      const int n_pairs = ((rows + kBMs - 1) / kBMs + 1) / 2;
+      const long long nsplit = (long long)n_pairs * a.B * a.Hq;
+      hipLaunchKernelGGL((fa_fwd_kernel<DT, D, true, false, true>), dim3((unsigned)nsplit), dim3(kThreads), 0,
+                         stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
+                         a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_pairs, vl, a.layout);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((fa_fwd_kernel<DT, D, CAUSAL, VARLEN, false>), dim3((unsigned)nblocks), dim3(kThreads), 0,
+                     stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                      a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_qt, vl, a.layout);
   return hipGetLastError();
 }
@@ -393,6 +487,11 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int set_fwd_schedule(int mode) {
+  if (mode != FA_SCHEDULE_AUTO && mode != FA_SCHEDULE_TILES && mode != FA_SCHEDULE_SPLIT) return -1;
+  return g_schedule.exchange(mode);
+}
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   return a.d == 128 ? launch_d<128>(a, stream) : launch_d<64>(a, stream);

@@ -70,6 +70,7 @@ constexpr int kDecodeTileRows = 128;
 constexpr int kFwdBlockRows = 256;  // query rows per prefill workgroup
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+int set_fwd_schedule(int mode);  // FA_SCHEDULE_*; previous mode or -1
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 // The static decode workspace behind fa_decode_noalloc (fa.h): its size and

@@ -351,6 +351,27 @@ fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_page
                           int num_pages, int page_size, int max_pages, int d, float scale,
                           int num_splits, int dtype, void* stream);
 
+/*
+ * fa_set_prefill_schedule - how the causal prefill entry points (fa_fwd,
+ * fa_fwd_strided) spread query tiles over workgroups. Results are the same
+ * up to the order of floating-point sums; only the work division changes.
+ *
+ *   FA_SCHEDULE_AUTO   (default) split when a causal grid of 256-row
+ *                      workgroups fits on the device at once, else tiles
+ *   FA_SCHEDULE_TILES  one 256-row query tile per workgroup, heaviest first
+ *   FA_SCHEDULE_SPLIT  one workgroup per pair of 128-row blocks (nb-1-p, p)
+ *                      of a head, the two halves of each key tile taken by
+ *                      two wave groups and joined by the merge identity of
+ *                      "The math of Flash Attention" (unite.ai)
+ *
+ * Process-wide, for all devices; takes effect at the next launch. Returns
+ * the previous mode, or -1 (and changes nothing) for an unknown mode.
+ */
+#define FA_SCHEDULE_AUTO 0
+#define FA_SCHEDULE_TILES 1
+#define FA_SCHEDULE_SPLIT 2
+int fa_set_prefill_schedule(int mode);
+
 /* Static text for a status code. */
 const char* fa_status_string(int status);
 

@@ -46,6 +46,19 @@ def test_status_strings():
     assert fa.fa_status_string(99) == "FA_UNKNOWN_STATUS"
 
 
+def test_prefill_schedule_knob():
+    # a host-side setting: no device is touched
+    prev = fa.fa_set_prefill_schedule(fa.FA_SCHEDULE_SPLIT)
+    try:
+        assert prev == fa.FA_SCHEDULE_AUTO
+        assert fa.fa_set_prefill_schedule(fa.FA_SCHEDULE_TILES) == fa.FA_SCHEDULE_SPLIT
+        for bad in (-1, 3, 99):
+            assert fa.fa_set_prefill_schedule(bad) == -1
+        assert fa.fa_set_prefill_schedule(fa.FA_SCHEDULE_AUTO) == fa.FA_SCHEDULE_TILES
+    finally:
+        fa.fa_set_prefill_schedule(fa.FA_SCHEDULE_AUTO)
+
+
 def fwd(**kw):
     a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, o=FAKE + 0x300000, lse=None,
              B=1, Hq=8, Hkv=8, Nq=128, Nk=128, d=64, scale=0.125, causal=0, dtype=0, stream=None)
