@@ -14,8 +14,8 @@
 //   fa_bwd_dkdv_kernel   one workgroup per (b, kv-head, 128 keys): each wave
 //                        keeps 32 keys' K and V in registers and dK^T, dV^T
 //                        accumulators, and walks the query tiles of every
-//                        q-head of its group (64 rows of Q, dO, LSE, delta
-//                        staged in LDS, double-buffered);
+//                        q-head of its group, tile-major (64 rows of Q, dO,
+//                        LSE, delta staged in LDS, double-buffered);
 //   fa_bwd_dq_kernel     one workgroup per (b, q-head, 128 query rows): each
 //                        wave keeps 32 rows' Q^T, dO^T operands and a dQ^T
 //                        accumulator, and walks the key tiles (64 rows of K
@@ -249,6 +249,17 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
   const int n_t = (Nq + kTileRows - 1) / kTileRows;
   const int per_head = max(0, n_t - t_first);
   const int total = grp * per_head;
+  // Visit order of the (query tile, q-head) pairs: tile-major with the
+  // group's q-heads innermost, so that the workgroups of one kv-head that
+  // run side by side (on one XCD: workgroup id L runs on XCD L % 8) read the
+  // same Q and dO tile at about the same time and it is fetched into that
+  // XCD's L2 once. The first half of the key blocks, dispatched first, walk
+  // the tiles down from the last one; the second half start as the first
+  // finish, the lightest first, and walk up from their first tile, which
+  // keeps them in step with each other as well.
+  const int n_kt = (Nk + kBwdKeyRows - 1) / kBwdKeyRows;
+  const bool down = kt < (n_kt + 1) / 2;
+  auto tile_of = [&](int it) { return down ? n_t - 1 - it / grp : t_first + it / grp; };
 
   // Q and dO tiles go HBM -> LDS directly (slot it & 1), one tile ahead; the
   // tile's LSE (log2 units) and delta go through one register of threads
@@ -256,7 +267,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)smem;
   float rl = 0.f;
   auto issue = [&](int it) {
-    const int h = g * grp + it / per_head, t = t_first + it % per_head;
+    const int h = g * grp + it % grp, t = tile_of(it);
     const size_t qo = ((size_t)b * Hq + h) * Nq;
     const int i0 = t * kTileRows;
     const int nvalid = min(kTileRows, Nq - i0);
@@ -288,7 +299,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
     const char* dot = qt + TILE;
     const float* l2 = reinterpret_cast<const float*>(qt + 2 * TILE);
     const float* dl = l2 + kTileRows;
-    const int i0 = (t_first + it % per_head) * kTileRows;
+    const int i0 = tile_of(it) * kTileRows;
     const int r0 = i0 + 32 * rh;  // first query row of this wave in the tile
     // skip a block entirely above the causal diagonal
     if (!CAUSAL || wk0 <= r0 + 31 + off) {
@@ -395,9 +406,12 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(
   constexpr int TILE = kTileRows * D * 2;
   __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];  // (K, V) x 2 buffers
 
-  const int nbh = B * Hq;
-  const int qt = n_qt - 1 - (int)(blockIdx.x / nbh), bh = blockIdx.x % nbh;  // last query tiles first
-  const int b = bh / Hq, h = bh % Hq, g = h / (Hq / Hkv);
+  // last query tiles first; one kv-head's workgroups on one XCD when the
+  // (batch, kv-head) pairs divide over the 8 XCDs, so its K and V are
+  // fetched into that XCD's L2 once
+  const Work wk = map_work(blockIdx.x, B, Hq, Hkv, n_qt);
+  const int qt = wk.qt, b = wk.b, h = wk.h, g = wk.g;
+  const int bh = b * Hq + h;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
   const int q0 = qt * kBwdQueryRows;
   const int q0w = q0 + 32 * wave;                  // first query row of this wave
