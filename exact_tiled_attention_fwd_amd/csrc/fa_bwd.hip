@@ -47,10 +47,20 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int kTileRows = 64;  // rows of a staged Q/dO (dK/dV kernel) or K/V (dQ kernel) tile
 
 // LDS tiles are row-major [64][D] 16-bit with 16-byte chunks XOR-swizzled by
-// row, so that the 32 rows a row-operand fetch touches spread over the banks.
+// row. The tiles are read both ways: as rows (one chunk column of 32 rows)
+// and transposed (ds_read_b64_tr_b16: 8 rows x 4 adjacent chunks). With
+// a = (row / 4) % 4 and e = row % 4 the XOR value is 4 (e ^ a) + a at
+// d = 128 (256-byte rows) and 4 ((row / 2) % 2 ^ a % 2) + a at d = 64
+// (128-byte rows, two to a bank row): a bijection of row % 16, so a chunk
+// column of 16 rows covers all 64 banks, and the 8 rows of a transposed read
+// fall on 4 different 4-chunk bank quads, each twice. Both reads are then
+// free of bank conflicts (the plain row % 16 XOR put a transposed read on 2
+// quads, 4 deep).
 template <int D>
 __device__ inline int chunk_pos(int row, int c) {
-  return D == 128 ? (c ^ (row & 15)) : (c ^ ((row >> 1) & 7));
+  const int a = (row >> 2) & 3;
+  if constexpr (D == 128) return c ^ (4 * ((row & 3) ^ a) + a);
+  else return c ^ ((4 * (((row >> 1) & 1) ^ (a & 1)) + a) & 7);
 }
 
 // Row operand (A of a rows x d product): row `row`, 8 elements from chunk c.
