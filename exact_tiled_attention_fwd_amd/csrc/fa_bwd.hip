@@ -187,10 +187,13 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_delta_kernel(const uint16_t* 
 }
 
 // ------------------------------------------------------------------ dK, dV
-// 8 waves: wave w owns keys 32 (w % 4) .. +31 of the workgroup's 128 and rows
-// 32 (w / 4) .. +31 of every 64-row query tile, so two waves (one per half
-// of the rows) accumulate partial dK, dV for the same keys; the halves are
-// added through LDS at the end.
+// 8 waves over 128 keys: wave w takes keys 32 (w % 4) .. +31 and, for S and
+// dP (and so P and dS), rows 32 (w / 4) .. +31 of every 64-row query tile.
+// The two waves of a key group split the accumulation: the first (w < 4)
+// adds dV^T over all 64 rows, the second dK^T; each hands the other, through
+// LDS, the half it lacks (the first its dS, the second its P). So a wave
+// keeps a single 32 x d accumulator, and the K and V rows of its keys stay in
+// registers as the B operands of S and dP.
 constexpr int kDkdvThreads = 512;
 
 template <int D>
@@ -201,6 +204,11 @@ __device__ inline uint32_t dma_off8(int i, int w, int lane, int nvalid) {  // 8 
   return (uint32_t)(min(row, nvalid - 1) * (D * 2) + chunk_pos<D>(row, pos) * 16);
 }
 
+template <bool V>
+struct BoolC {
+  static constexpr bool value = V;
+};
+
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -210,11 +218,10 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
   constexpr int KS = D / 16, MT = D / 32;
   constexpr int TILE = kTileRows * D * 2;
   constexpr int BUF = 2 * TILE + 2 * kTileRows * 4;  // Q, dO, lse2, delta
-  constexpr int KL_BYTES = kBwdKeyRows * D * 2;      // K rows of the workgroup's keys
-  constexpr int RED = MT * 16 * 256 * 4;             // one accumulator set of 4 waves
-  constexpr int SMEM = 2 * BUF + KL_BYTES > RED ? 2 * BUF + KL_BYTES : RED;
-  __shared__ __attribute__((aligned(16))) char smem[SMEM];
-  char* const kls = smem + 2 * BUF;
+  constexpr int NBUF = 2;                            // staged query tiles: this one, the next
+  constexpr int XW = 2 * 64 * 16;                    // a wave's packed P or dS: 2 x 16 bytes per lane
+  __shared__ __attribute__((aligned(16))) char smem[NBUF * BUF + 8 * XW];
+  char* const xch = smem + NBUF * BUF;               // [wave][2][64 lanes][16 bytes]
 
   const int nbg = B * Hkv;
   const int kt = blockIdx.x / nbg, bg = blockIdx.x % nbg;  // key tiles from the first: heaviest first
@@ -222,35 +229,26 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform for the scalar LDS address
   const int kw = wave & 3, rh = wave >> 2;               // key group, row half of each tile
+  const bool dv_wave = (wv >> 2) == 0;                   // accumulates dV (else dK)
   const int kt0 = kt * kBwdKeyRows;
   const int wk0 = kt0 + 32 * kw;                         // first key of this wave
   const int key = wk0 + (lane & 31);                     // this lane's key column
   const int off = Nk - Nq;                               // causal: key j visible to query i iff j <= i + off
 
-  // V rows of this wave's 32 keys in registers (B operand of dP = dO V^T);
-  // the K rows of all 128 keys in LDS (B operand of S = Q K^T, read per use).
+  // K and V rows of this wave's 32 keys: the B operands of S = Q K^T and dP = dO V^T.
   const size_t kvo = (size_t)bg * Nk * D;
   const int krow = min(key, Nk - 1);
-  u32x4 vop[KS];
+  u32x4 kop[KS], vop[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
+  for (int ks = 0; ks < KS; ++ks) {
+    kop[ks] = *reinterpret_cast<const u32x4*>(k + kvo + (size_t)krow * D + 16 * ks + 8 * half);
     vop[ks] = *reinterpret_cast<const u32x4*>(v + kvo + (size_t)krow * D + 16 * ks + 8 * half);
-  {
-    constexpr int CPR = D / 8;
-#pragma unroll
-    for (int p = 0; p < kBwdKeyRows * CPR / kDkdvThreads; ++p) {
-      const int idx = threadIdx.x + kDkdvThreads * p;
-      const int row = idx / CPR, c = idx % CPR;
-      const int src = min(kt0 + row, Nk - 1);
-      *reinterpret_cast<u32x4*>(kls + row * (D * 2) + chunk_pos<D>(row, c) * 16) =
-          *reinterpret_cast<const u32x4*>(k + kvo + (size_t)src * D + c * 8);
-    }
   }
-  f32x16 acc_dk[MT], acc_dv[MT];
+  f32x16 acc[MT];  // dV^T or dK^T of this wave's keys
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc_dk[mt][r] = acc_dv[mt][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
 
   // Query tiles that see at least one key of this workgroup, for every
   // q-head of the group.
@@ -271,12 +269,12 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
   const bool down = kt < (n_kt + 1) / 2;
   auto tile_of = [&](int it) { return down ? n_t - 1 - it / grp : t_first + it / grp; };
 
-  // Q and dO tiles go HBM -> LDS directly (slot it & 1), one tile ahead; the
+  // Q and dO tiles go HBM -> LDS directly (slot it % 2), one tile ahead; the
   // tile's LSE (log2 units) and delta go through one register of threads
   // 0..127. Each wave waits for its own loads before the tile barrier.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)smem;
   float rl = 0.f;
-  auto issue = [&](int it) {
+  auto issue = [&](int it, int slot) {
     const int h = g * grp + it % grp, t = tile_of(it);
     const size_t qo = ((size_t)b * Hq + h) * Nq;
     const int i0 = t * kTileRows;
@@ -284,51 +282,120 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const uint16_t* base = (u ? dout : q) + (qo + i0) * D;
-      const uint32_t slot = lds0 + (uint32_t)((it & 1) * BUF + u * TILE + 64 * wv * 16);
+      const uint32_t dst = lds0 + (uint32_t)(slot * BUF + u * TILE + 64 * wv * 16);
 #pragma unroll
-      for (int i = 0; i < TILE / 8192; ++i) dma16(base, dma_off8<D>(i, wv, lane, nvalid), slot + 8192 * i);
+      for (int i = 0; i < TILE / 8192; ++i) dma16(base, dma_off8<D>(i, wv, lane, nvalid), dst + 8192 * i);
     }
     if (threadIdx.x < kTileRows)
       rl = lse2_of(lse + qo + i0, threadIdx.x, Nq - i0);
     else if (threadIdx.x < 2 * kTileRows)
       rl = (i0 + (int)threadIdx.x - kTileRows < Nq) ? delta[qo + i0 + threadIdx.x - kTileRows] : 0.f;
   };
-  auto put_rl = [&](int it) {
-    if (threadIdx.x < 2 * kTileRows) reinterpret_cast<float*>(smem + (it & 1) * BUF + 2 * TILE)[threadIdx.x] = rl;
+  auto put_rl = [&](int slot) {
+    if (threadIdx.x < 2 * kTileRows) reinterpret_cast<float*>(smem + slot * BUF + 2 * TILE)[threadIdx.x] = rl;
   };
 
-  if (total > 0) {
-    issue(0);
-    put_rl(0);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
-  for (int it = 0; it < total; ++it) {
-    if (it + 1 < total) issue(it + 1);
-    const char* qt = smem + (it & 1) * BUF;
-    const char* dot = qt + TILE;
-    const float* l2 = reinterpret_cast<const float*>(qt + 2 * TILE);
-    const float* dl = l2 + kTileRows;
-    const int i0 = tile_of(it) * kTileRows;
-    const int r0 = i0 + 32 * rh;  // first query row of this wave in the tile
-    // skip a block entirely above the causal diagonal
-    if (!CAUSAL || wk0 <= r0 + 31 + off) {
-      f32x16 s, dp;
+  // Lane offsets (bytes in a [64][D] tile) of the operand reads: the row
+  // operand (row 32 RH + lane % 32, chunk 2 ks + half) and the transposed
+  // operand of 16-row group 0 (tr_op's pattern); group G adds 16 G rows,
+  // since the swizzle depends on the row only through row % 16.
+  auto row_off = [&](int rh_, int ks) {
+    const int row = 32 * rh_ + (lane & 31);
+    return (uint32_t)(row * (D * 2) + chunk_pos<D>(row, 2 * ks + half) * 16);
+  };
+  uint32_t tro[MT][2];
+  {
+    const int gi = lane >> 4, e = (lane >> 2) & 3, qq = lane & 3;
+    const int hh = gi >> 1, dh = gi & 1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma32<DT>(row_op<D>(qt, 32 * rh + (lane & 31), 2 * ks + half),
-                       row_op<D>(kls, 32 * kw + (lane & 31), 2 * ks + half), s);
-        dp = mfma32<DT>(row_op<D>(dot, 32 * rh + (lane & 31), 2 * ks + half), vop[ks], dp);
+      for (int p2 = 0; p2 < 2; ++p2) {
+        const int row = 8 * p2 + 4 * hh + e, c = 4 * mt + 2 * dh + (qq >> 1);
+        tro[mt][p2] = (uint32_t)(row * (D * 2) + chunk_pos<D>(row, c) * 16 + 8 * (qq & 1));
       }
-      // masking only where this wave's keys reach past its first row or Nk
+  }
+
+  constexpr int NU = 4 * MT, NM = 2 * KS, PF = 4;
+  uint32_t own[8], oth[8];  // packed B operands of U: this wave's half, the partner's half
+  f32x16 s, dp;
+
+  // The loop for the waves of row half RH (0: accumulate dV, 1: dK).
+  auto run = [&](auto rhc) {
+    constexpr int RH = decltype(rhc)::value ? 1 : 0;
+    uint32_t rwo[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) rwo[ks] = row_off(RH, ks);
+
+    // Matrix-core phases: M = S and dP of this wave's rows of the tile (2 KS
+    // ops, A = Q and dO rows, alternating), U = the dV^T (or dK^T) update over
+    // both row halves (2 x 2 x MT ops, A = dO^T (or Q^T) read transposed). A
+    // operands come through a ring of 4 registers, fetched 4 ops ahead.
+    auto phase = [&](auto do_u, const char* tile) {
+      constexpr bool DU = decltype(do_u)::value;
+      constexpr int N = DU ? NU : NM;
+      const char* tsrc = tile + (RH == 0 ? TILE : 0);  // dO^T for dV, Q^T for dK
+      auto read = [&](int t) -> u32x4 {
+        if constexpr (DU) {
+          const int h = t / (2 * MT), G = (t / MT) % 2, mt = t % MT;
+          const char* tg = tsrc + (2 * h + G) * 16 * (D * 2);
+          u32x4 out;
+#pragma unroll
+          for (int p2 = 0; p2 < 2; ++p2) {
+            const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tg + tro[mt][p2]));
+            const u32x2 w = __builtin_bit_cast(u32x2, x);
+            out[2 * p2] = w[0];
+            out[2 * p2 + 1] = w[1];
+          }
+          return out;
+        } else {
+          return *reinterpret_cast<const u32x4*>(tile + ((t & 1) ? TILE : 0) + rwo[t >> 1]);
+        }
+      };
+      u32x4 buf[PF];
+#pragma unroll
+      for (int t = 0; t < PF; ++t) buf[t] = read(t);
+      if constexpr (!DU) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int t = 0; t < N; ++t) {
+        const u32x4 a = buf[t % PF];
+        if (t + PF < N) buf[t % PF] = read(t + PF);
+        if constexpr (DU) {
+          const int h = t / (2 * MT), G = (t / MT) % 2, mt = t % MT;
+          const uint32_t* bsrc = (h == RH) ? own : oth;
+          const u32x4 bb = {bsrc[4 * G], bsrc[4 * G + 1], bsrc[4 * G + 2], bsrc[4 * G + 3]};
+          acc[mt] = mfma32<DT>(a, bb, acc[mt]);
+        } else {
+          if (t & 1)
+            dp = mfma32<DT>(a, vop[t >> 1], dp);
+          else
+            s = mfma32<DT>(a, kop[t >> 1], s);
+        }
+      }
+      // keep the order: the first PF operands' reads, then each MFMA
+      // followed by the reads of the operand PF ahead
+      __builtin_amdgcn_sched_group_barrier(0x100, DU ? 2 * PF : PF, 0);
+#pragma unroll
+      for (int t = 0; t < N; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (t + PF < N) __builtin_amdgcn_sched_group_barrier(0x100, DU ? 2 : 1, 0);
+      }
+    };
+
+    // P and dS of this wave's rows (register r holds query row 32 RH +
+    // acc_key(r, half) of the tile); keeps one, hands the other to the partner.
+    auto softmax = [&](const char* tile, int i0) {
+      const float* l2 = reinterpret_cast<const float*>(tile + 2 * TILE);
+      const float* dl = l2 + kTileRows;
+      const int r0 = i0 + 32 * RH;
       const bool need_mask = (wk0 + 31 >= Nk) || (CAUSAL && wk0 + 31 > r0 + off);
-      // P and dS; register r holds query row 32 rh + acc_key(r, half) of the tile.
       uint32_t pk[8], dsk[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const int rl0 = 32 * rh + 8 * m + 4 * half;
+        const int rl0 = 32 * RH + 8 * m + 4 * half;
         const f32x4 L = *reinterpret_cast<const f32x4*>(l2 + rl0);
         const f32x4 Dv = *reinterpret_cast<const f32x4*>(dl + rl0);
         float p[4], ds[4];
@@ -348,61 +415,84 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
         dsk[2 * m] = pack2<DT>(ds[0], ds[1]);
         dsk[2 * m + 1] = pack2<DT>(ds[2], ds[3]);
       }
-      // dV^T += dO^T P, dK^T += Q^T dS over this wave's 32 rows
+      const uint32_t* give = RH == 0 ? dsk : pk;
+      char* xw = xch + wv * XW + lane * 16;
 #pragma unroll
-      for (int G = 0; G < 2; ++G) {
-        const u32x4 bp = {pk[4 * G], pk[4 * G + 1], pk[4 * G + 2], pk[4 * G + 3]};
-        const u32x4 bs = {dsk[4 * G], dsk[4 * G + 1], dsk[4 * G + 2], dsk[4 * G + 3]};
+      for (int u = 0; u < 2; ++u)
+        *reinterpret_cast<u32x4*>(xw + 1024 * u) = u32x4{give[4 * u], give[4 * u + 1], give[4 * u + 2], give[4 * u + 3]};
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          acc_dv[mt] = mfma32<DT>(tr_op<D>(dot, 2 * rh + G, mt, lane), bp, acc_dv[mt]);
-          acc_dk[mt] = mfma32<DT>(tr_op<D>(qt, 2 * rh + G, mt, lane), bs, acc_dk[mt]);
-        }
+      for (int j = 0; j < 8; ++j) own[j] = RH == 0 ? pk[j] : dsk[j];
+    };
+
+    // Two barriers per tile: S, dP and the softmax of this wave's rows, whose
+    // half for the partner goes to the exchange buffer; a barrier; U over both
+    // halves; the tile barrier, which also waits for the next tile's loads.
+    // Those go to the other slot, whose last reads (the previous tile's U)
+    // ended before the previous tile barrier; the exchange buffer is rewritten
+    // only after the tile barrier that follows its last read.
+    int cur = 0;
+    for (int it = 0; it < total; ++it) {
+      const int nxt = cur ^ 1;
+      if (it + 1 < total) issue(it + 1, nxt);
+      const int i0 = tile_of(it) * kTileRows;
+      // a row half sees these keys unless it lies entirely above the causal diagonal
+      const bool a_lo = !CAUSAL || wk0 <= i0 + 31 + off, a_hi = !CAUSAL || wk0 <= i0 + 63 + off;
+      const bool a_own = RH ? a_hi : a_lo, a_oth = RH ? a_lo : a_hi;
+      const char* tile = smem + cur * BUF;
+      if (a_own) {
+        phase(BoolC<false>{}, tile);
+        softmax(tile, i0);
       }
+      __syncthreads();  // the exchange is written
+      if (a_own || a_oth) {
+        if (a_oth) {
+          const char* xr = xch + (wv ^ 4) * XW + lane * 16;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(xr + 1024 * u);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) oth[4 * u + j] = w[j];
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) oth[j] = 0u;
+        }
+        if (!a_own) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) own[j] = 0u;
+        }
+        phase(BoolC<true>{}, tile);
+      }
+      if (it + 1 < total) put_rl(nxt);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile it + 1 has landed
+      __syncthreads();
+      cur = nxt;
     }
-    if (it + 1 < total) put_rl(it + 1);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile it + 1 has landed
-    __syncthreads();
-  }
-
-  // Add the two row halves' partial sums (through LDS, register-major so a
-  // register of all 256 lanes of a half is one contiguous row), then write.
-  // acc register r of block mt holds d = 32 mt + acc_key(r, half) of this key.
-  float* red = reinterpret_cast<float*>(smem);
-  const int rlane = kw * 64 + lane;
-  auto reduce = [&](f32x16 (&acc)[MT]) {
-    if (rh == 1) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) red[(mt * 16 + r) * 256 + rlane] = acc[mt][r];
-    }
-    __syncthreads();
-    if (rh == 0) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mt][r] += red[(mt * 16 + r) * 256 + rlane];
-    }
-    __syncthreads();
   };
-  reduce(acc_dk);
-  reduce(acc_dv);
 
-  if (rh != 0 || key >= Nk) return;
-  uint16_t* dkr = dk + kvo + (size_t)key * D;
-  uint16_t* dvr = dv + kvo + (size_t)key * D;
+  if (total > 0) {
+    issue(0, 0);
+    put_rl(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  if (dv_wave)
+    run(BoolC<false>{});
+  else
+    run(BoolC<true>{});
+
+  // acc register r of block mt holds d = 32 mt + acc_key(r, half) of this key.
+  if (key >= Nk) return;
+  uint16_t* row = (dv_wave ? dv : dk) + kvo + (size_t)key * D;
+  const float f = dv_wave ? 1.f : scale;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int d0 = 32 * mt + 8 * m + 4 * half;
-      const u32x2 wk = {pack2<DT>(acc_dk[mt][4 * m] * scale, acc_dk[mt][4 * m + 1] * scale),
-                        pack2<DT>(acc_dk[mt][4 * m + 2] * scale, acc_dk[mt][4 * m + 3] * scale)};
-      const u32x2 wvv = {pack2<DT>(acc_dv[mt][4 * m], acc_dv[mt][4 * m + 1]),
-                         pack2<DT>(acc_dv[mt][4 * m + 2], acc_dv[mt][4 * m + 3])};
-      *reinterpret_cast<u32x2*>(dkr + d0) = wk;
-      *reinterpret_cast<u32x2*>(dvr + d0) = wvv;
+      const u32x2 w = {pack2<DT>(acc[mt][4 * m] * f, acc[mt][4 * m + 1] * f),
+                       pack2<DT>(acc[mt][4 * m + 2] * f, acc[mt][4 * m + 3] * f)};
+      *reinterpret_cast<u32x2*>(row + d0) = w;
     }
 }
 
