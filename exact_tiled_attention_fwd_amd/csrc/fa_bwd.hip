@@ -218,10 +218,10 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
   constexpr int KS = D / 16, MT = D / 32;
   constexpr int TILE = kTileRows * D * 2;
   constexpr int BUF = 2 * TILE + 2 * kTileRows * 4;  // Q, dO, lse2, delta
-  constexpr int NBUF = 2;                            // staged query tiles: this one, the next
+  constexpr int NBUF = 3;                            // staged query tiles: previous, this, next
   constexpr int XW = 2 * 64 * 16;                    // a wave's packed P or dS: 2 x 16 bytes per lane
-  __shared__ __attribute__((aligned(16))) char smem[NBUF * BUF + 8 * XW];
-  char* const xch = smem + NBUF * BUF;               // [wave][2][64 lanes][16 bytes]
+  __shared__ __attribute__((aligned(16))) char smem[NBUF * BUF + 2 * 8 * XW];
+  char* const xch = smem + NBUF * BUF;               // [tile parity][wave][2][64 lanes][16 bytes]
 
   const int nbg = B * Hkv;
   const int kt = blockIdx.x / nbg, bg = blockIdx.x % nbg;  // key tiles from the first: heaviest first
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
   const bool down = kt < (n_kt + 1) / 2;
   auto tile_of = [&](int it) { return down ? n_t - 1 - it / grp : t_first + it / grp; };
 
-  // Q and dO tiles go HBM -> LDS directly (slot it % 2), one tile ahead; the
+  // Q and dO tiles go HBM -> LDS directly (slot it % 3), one tile ahead; the
   // tile's LSE (log2 units) and delta go through one register of threads
   // 0..127. Each wave waits for its own loads before the tile barrier.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)smem;
@@ -318,6 +318,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
 
   constexpr int NU = 4 * MT, NM = 2 * KS, PF = 4;
   uint32_t own[8], oth[8];  // packed B operands of U: this wave's half, the partner's half
+  uint32_t fresh[8];        // this wave's half of the tile just softmaxed
   f32x16 s, dp;
 
   // The loop for the waves of row half RH (0: accumulate dV, 1: dK).
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
 
     // P and dS of this wave's rows (register r holds query row 32 RH +
     // acc_key(r, half) of the tile); keeps one, hands the other to the partner.
-    auto softmax = [&](const char* tile, int i0) {
+    auto softmax = [&](const char* tile, int i0, int it) {
       const float* l2 = reinterpret_cast<const float*>(tile + 2 * TILE);
       const float* dl = l2 + kTileRows;
       const int r0 = i0 + 32 * RH;
@@ -416,58 +417,75 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
         dsk[2 * m + 1] = pack2<DT>(ds[2], ds[3]);
       }
       const uint32_t* give = RH == 0 ? dsk : pk;
-      char* xw = xch + wv * XW + lane * 16;
+      char* xw = xch + ((it & 1) * 8 + wv) * XW + lane * 16;
 #pragma unroll
       for (int u = 0; u < 2; ++u)
         *reinterpret_cast<u32x4*>(xw + 1024 * u) = u32x4{give[4 * u], give[4 * u + 1], give[4 * u + 2], give[4 * u + 3]};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) own[j] = RH == 0 ? pk[j] : dsk[j];
+      for (int j = 0; j < 8; ++j) fresh[j] = RH == 0 ? pk[j] : dsk[j];
     };
 
-    // Two barriers per tile: S, dP and the softmax of this wave's rows, whose
-    // half for the partner goes to the exchange buffer; a barrier; U over both
-    // halves; the tile barrier, which also waits for the next tile's loads.
-    // Those go to the other slot, whose last reads (the previous tile's U)
-    // ended before the previous tile barrier; the exchange buffer is rewritten
-    // only after the tile barrier that follows its last read.
-    int cur = 0;
+    // U of tile j: both row halves' P (or dS), this wave's from registers,
+    // the partner's from the exchange buffer of parity j & 1 (zero for a row
+    // half that sees none of these keys).
+    auto update = [&](int j, bool j_own, bool j_oth, const char* tile) {
+      if (j_oth) {
+        const char* xr = xch + ((j & 1) * 8 + (wv ^ 4)) * XW + lane * 16;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(xr + 1024 * u);
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) oth[4 * u + q2] = w[q2];
+        }
+      } else {
+#pragma unroll
+        for (int q2 = 0; q2 < 8; ++q2) oth[q2] = 0u;
+      }
+      if (!j_own) {
+#pragma unroll
+        for (int q2 = 0; q2 < 8; ++q2) own[q2] = 0u;
+      }
+      phase(BoolC<true>{}, tile);
+    };
+
+    // One barrier per tile. In the interval of tile it a wave runs S, dP and
+    // the softmax of tile it (its half for the partner to the exchange
+    // buffer of parity it & 1) and U of tile it - 1; the two waves of a key
+    // group, which share a SIMD, take these in opposite orders (row half 0:
+    // S first), so that one's vector work meets the other's matrix-core
+    // work. Tiles it - 1, it and it + 1 (in flight) are in use at once: three
+    // slots; the loads of tile it + 1 go to the slot of tile it - 2, last
+    // read by U in the previous interval. The exchange buffer of a parity is
+    // written in one interval, read in the next and rewritten in the one
+    // after, each across a barrier.
+    int cur = 0, prv = 0;
+    bool p_own = false, p_oth = false;  // the previous tile's row halves see these keys
     for (int it = 0; it < total; ++it) {
-      const int nxt = cur ^ 1;
+      const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
       if (it + 1 < total) issue(it + 1, nxt);
       const int i0 = tile_of(it) * kTileRows;
       // a row half sees these keys unless it lies entirely above the causal diagonal
       const bool a_lo = !CAUSAL || wk0 <= i0 + 31 + off, a_hi = !CAUSAL || wk0 <= i0 + 63 + off;
       const bool a_own = RH ? a_hi : a_lo, a_oth = RH ? a_lo : a_hi;
       const char* tile = smem + cur * BUF;
+      const bool do_u = it > 0 && (p_own || p_oth);
+      if (RH == 1 && do_u) update(it - 1, p_own, p_oth, smem + prv * BUF);
       if (a_own) {
         phase(BoolC<false>{}, tile);
-        softmax(tile, i0);
+        softmax(tile, i0, it);
       }
-      __syncthreads();  // the exchange is written
-      if (a_own || a_oth) {
-        if (a_oth) {
-          const char* xr = xch + (wv ^ 4) * XW + lane * 16;
+      if (RH == 0 && do_u) update(it - 1, p_own, p_oth, smem + prv * BUF);
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(xr + 1024 * u);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) oth[4 * u + j] = w[j];
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) oth[j] = 0u;
-        }
-        if (!a_own) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) own[j] = 0u;
-        }
-        phase(BoolC<true>{}, tile);
-      }
+      for (int q2 = 0; q2 < 8; ++q2) own[q2] = fresh[q2];
+      p_own = a_own;
+      p_oth = a_oth;
       if (it + 1 < total) put_rl(nxt);
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile it + 1 has landed
       __syncthreads();
+      prv = cur;
       cur = nxt;
     }
+    if (total > 0 && (p_own || p_oth)) update(total - 1, p_own, p_oth, smem + prv * BUF);
   };
 
   if (total > 0) {
