@@ -267,15 +267,15 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
   // keeps them in step with each other as well.
   const int n_kt = (Nk + kBwdKeyRows - 1) / kBwdKeyRows;
   const bool down = kt < (n_kt + 1) / 2;
-  auto tile_of = [&](int it) { return down ? n_t - 1 - it / grp : t_first + it / grp; };
+  auto tile_at = [&](int ti) { return down ? n_t - 1 - ti : t_first + ti; };  // ti-th tile visited
 
   // Q and dO tiles go HBM -> LDS directly (slot it % 3), one tile ahead; the
   // tile's LSE (log2 units) and delta go through one register of threads
   // 0..127. Each wave waits for its own loads before the tile barrier.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)smem;
   float rl = 0.f;
-  auto issue = [&](int it, int slot) {
-    const int h = g * grp + it % grp, t = tile_of(it);
+  auto issue = [&](int t, int hg, int slot) {  // query tile t of q-head hg of the group
+    const int h = g * grp + hg;
     const size_t qo = ((size_t)b * Hq + h) * Nq;
     const int i0 = t * kTileRows;
     const int nvalid = min(kTileRows, Nq - i0);
@@ -459,11 +459,17 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
     // written in one interval, read in the next and rewritten in the one
     // after, each across a barrier.
     int cur = 0, prv = 0;
+    int ti = 0, hg = 0;                 // visit position of tile it: tile index, q-head in the group
     bool p_own = false, p_oth = false;  // the previous tile's row halves see these keys
     for (int it = 0; it < total; ++it) {
       const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
-      if (it + 1 < total) issue(it + 1, nxt);
-      const int i0 = tile_of(it) * kTileRows;
+      int ti_n = ti, hg_n = hg + 1;
+      if (hg_n == grp) {
+        hg_n = 0;
+        ++ti_n;
+      }
+      if (it + 1 < total) issue(tile_at(ti_n), hg_n, nxt);
+      const int i0 = tile_at(ti) * kTileRows;
       // a row half sees these keys unless it lies entirely above the causal diagonal
       const bool a_lo = !CAUSAL || wk0 <= i0 + 31 + off, a_hi = !CAUSAL || wk0 <= i0 + 63 + off;
       const bool a_own = RH ? a_hi : a_lo, a_oth = RH ? a_lo : a_hi;
@@ -484,12 +490,14 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
       __syncthreads();
       prv = cur;
       cur = nxt;
+      ti = ti_n;
+      hg = hg_n;
     }
     if (total > 0 && (p_own || p_oth)) update(total - 1, p_own, p_oth, smem + prv * BUF);
   };
 
   if (total > 0) {
-    issue(0, 0);
+    issue(tile_at(0), 0, 0);
     put_rl(0);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -576,6 +584,86 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(
       for (int i = 0; i < TILE / 4096; ++i) dma16(base, dma_off<D>(i, wv, lane, nvalid), slot + 4096 * i);
     }
   };
+
+  // Lane offsets (bytes in a [64][D] tile) of the operand reads: K or V rows
+  // lane % 32 (+ 32 kb, a constant), chunk 2 ks + half; K^T transposed as
+  // tr_op reads it for 16-row group 0 (group G adds 16 G rows, since the
+  // swizzle depends on the row only through row % 16).
+  uint32_t rwo[KS], tro[MT][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    rwo[ks] = (uint32_t)((lane & 31) * (D * 2) + chunk_pos<D>(lane & 31, 2 * ks + half) * 16);
+  {
+    const int gi = lane >> 4, e = (lane >> 2) & 3, qq = lane & 3;
+    const int hh = gi >> 1, dh = gi & 1;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int p2 = 0; p2 < 2; ++p2) {
+        const int row = 8 * p2 + 4 * hh + e, c = 4 * mt + 2 * dh + (qq >> 1);
+        tro[mt][p2] = (uint32_t)(row * (D * 2) + chunk_pos<D>(row, c) * 16 + 8 * (qq & 1));
+      }
+  }
+
+  // Matrix-core phases, A operands through a ring of PF registers fetched PF
+  // ops ahead (the first PF reads pinned ahead of the first MFMA):
+  //   SD(kb): S^T and dP^T of 32-key block kb (2 KS ops, A = K and V rows,
+  //           alternating; B = Q^T, dO^T in registers);
+  //   DQ:     dQ^T += K^T dS^T (4 x MT ops, A = K^T transposed).
+  constexpr int PF = 4;
+  f32x16 s, dp;
+  uint32_t dsk[2][8];
+  auto phase = [&](auto is_dq, const char* kt, const char* vt, int kb) {
+    constexpr bool DQ = decltype(is_dq)::value;
+    constexpr int N = DQ ? 4 * MT : 2 * KS;
+    auto read = [&](int t) -> u32x4 {
+      if constexpr (DQ) {
+        const int G = t / MT, mt = t % MT;
+        const char* tg = kt + G * 16 * (D * 2);
+        u32x4 out;
+#pragma unroll
+        for (int p2 = 0; p2 < 2; ++p2) {
+          const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(tg + tro[mt][p2]));
+          const u32x2 w = __builtin_bit_cast(u32x2, x);
+          out[2 * p2] = w[0];
+          out[2 * p2 + 1] = w[1];
+        }
+        return out;
+      } else {
+        return *reinterpret_cast<const u32x4*>(((t & 1) ? vt : kt) + kb * 32 * (D * 2) + rwo[t >> 1]);
+      }
+    };
+    u32x4 buf[PF];
+#pragma unroll
+    for (int t = 0; t < PF; ++t) buf[t] = read(t);
+    if constexpr (!DQ) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < N; ++t) {
+      const u32x4 a = buf[t % PF];
+      if (t + PF < N) buf[t % PF] = read(t + PF);
+      if constexpr (DQ) {
+        const int G = t / MT, mt = t % MT;
+        const int kb2 = G >> 1, o4 = 4 * (G & 1);
+        const u32x4 bs = {dsk[kb2][o4], dsk[kb2][o4 + 1], dsk[kb2][o4 + 2], dsk[kb2][o4 + 3]};
+        acc[mt] = mfma32<DT>(a, bs, acc[mt]);
+      } else {
+        if (t & 1)
+          dp = mfma32<DT>(a, dop[t >> 1], dp);
+        else
+          s = mfma32<DT>(a, qop[t >> 1], s);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, DQ ? 2 * PF : PF, 0);
+#pragma unroll
+    for (int t = 0; t < N; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (t + PF < N) __builtin_amdgcn_sched_group_barrier(0x100, DQ ? 2 : 1, 0);
+    }
+  };
+
   if (n_kv > 0) issue(0);
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): Q, dO operands and tile 0
   __syncthreads();
@@ -583,48 +671,29 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(
     if (j + 1 < n_kv) issue(j + 1);
     const char* kt = smem + (j & 1) * 2 * TILE;
     const char* vt = kt + TILE;
-    // S^T = K Q^T and dP^T = V dO^T for both 32-key blocks (four chains)
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = mfma32<DT>(row_op<D>(kt, 32 * kb + (lane & 31), 2 * ks + half), qop[ks], s[kb]);
-        dp[kb] = mfma32<DT>(row_op<D>(vt, 32 * kb + (lane & 31), 2 * ks + half), dop[ks], dp[kb]);
-      }
     // masking only on the causal diagonal or a ragged last tile
     const bool need_mask = (j * kTileRows + kTileRows > Nk) || (CAUSAL && j * kTileRows + kTileRows - 1 > q0w + off);
-    uint32_t dsk[2][8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      phase(BoolC<false>{}, kt, vt, kb);
       // register r holds key j*64 + 32 kb + acc_key(r, half) of this lane's query
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float ds[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          float x = exp2_fast(__builtin_fmaf(s[kb][r + u], c2, -l2));
+          float x = exp2_fast(__builtin_fmaf(s[r + u], c2, -l2));
           if (need_mask) {
             const int key = j * kTileRows + 32 * kb + acc_key(r + u, half);
             const bool hide = (key >= Nk) | (CAUSAL & (key > qrow + off));
             x = hide ? 0.f : x;
           }
-          ds[u] = x * (dp[kb][r + u] - dl);
+          ds[u] = x * (dp[r + u] - dl);
         }
         dsk[kb][r >> 1] = pack2<DT>(ds[0], ds[1]);
       }
     }
-#pragma unroll
-    for (int G = 0; G < 4; ++G) {
-      const int kb = G >> 1, o4 = 4 * (G & 1);
-      const u32x4 bs = {dsk[kb][o4], dsk[kb][o4 + 1], dsk[kb][o4 + 2], dsk[kb][o4 + 3]};
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32<DT>(tr_op<D>(kt, G, mt, lane), bs, acc[mt]);
-    }
+    phase(BoolC<true>{}, kt, vt, 0);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile j + 1 has landed
     __syncthreads();
   }
