@@ -22,6 +22,7 @@ pytestmark = pytest.mark.gpu
 
 REL_L2 = 1e-2
 MAX_ABS_FRAC = 2e-2
+ZERO_REF_ABS = 1e-4
 
 
 def run_gpu(fa, x, do_bits, causal):
@@ -49,9 +50,18 @@ def check_grads(got, ref, what):
         top = float(np.abs(r).max())
         print(f"[parity] {what} {name}: rel_l2={rel:.3e} max_abs={mx:.3e} max_ref={top:.3e}", file=sys.stderr,
               flush=True)
+        if top == 0.0:
+            # An exactly zero gradient (one visible key: P = 1, so dS = dP -
+            # delta = 0) has no relative scale. What is left is the fp32
+            # difference of two summation orders of one d-term dot product
+            # (dO . V in the MFMA against dO . O in the delta kernel, O = V):
+            # below d 2^-24 sum |dO V|, under 1e-4 for N(0,1) inputs.
+            if mx > ZERO_REF_ABS:
+                bad.append(f"{name}: max-abs {mx} against an exactly zero reference")
+            continue
         if rel > REL_L2:
             bad.append(f"{name}: rel-L2 {rel}")
-        if mx > MAX_ABS_FRAC * max(top, 1e-30):
+        if mx > MAX_ABS_FRAC * top:
             bad.append(f"{name}: max-abs {mx} vs max |ref| {top}")
     assert not bad, f"{what}: " + "; ".join(bad)
 
@@ -64,6 +74,12 @@ CASES = [
     (1, 8, 2, 150, 400, 128, ai.BF16, True),     # causal Nq < Nk (chunked prefill)
     (1, 4, 4, 513, 513, 64, ai.BF16, True),
     (1, 4, 1, 257, 1000, 128, ai.FP16, False),
+    # dK/dV splits each key group's accumulation between two waves and hands
+    # P / dS over through LDS; a row half above the diagonal counts as zero
+    (1, 2, 1, 1, 1, 64, ai.FP16, True),          # one row, one key
+    (2, 6, 2, 77, 77, 128, ai.BF16, True),       # three q-heads per kv-head, one ragged tile
+    (1, 4, 2, 640, 1100, 64, ai.FP16, True),     # causal Nq < Nk, ragged key blocks
+    (1, 2, 2, 1000, 1000, 128, ai.FP16, True),   # key blocks walking down and up
 ]
 
 
