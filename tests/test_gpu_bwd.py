@@ -96,6 +96,36 @@ def test_bwd_vs_oracle(fa, case):
     check_grads([from_dev(t, dt) for t in (dq, dk, dv)], ref, f"bwd {case}")
 
 
+def _random_bwd_cases(n=10, seed=47):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4]))
+        Hq = Hkv * int(rng.choice([1, 2, 3, 4]))
+        Nk = int(rng.integers(1, 900))
+        causal = bool(rng.random() < 0.6)
+        Nq = int(rng.integers(1, Nk + 1)) if causal else int(rng.integers(1, 900))
+        dt = ai.BF16 if rng.random() < 0.5 else ai.FP16
+        cases.append((640 + i, int(rng.integers(1, 3)), Hq, Hkv, Nq, Nk, d, dt, causal))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_bwd_cases(),
+                         ids=lambda c: f"s{c[0]}B{c[1]}Hq{c[2]}Hkv{c[3]}Nq{c[4]}Nk{c[5]}d{c[6]}{c[7]}{'c' if c[8] else 'n'}")
+def test_bwd_random_shapes(fa, case):
+    # Seeded shapes: ragged query and key tails, GQA groups of 1-4 (3 too),
+    # causal with Nq <= Nk, both head widths and 16-bit types.
+    seed, B, Hq, Hkv, Nq, Nk, d, dt, causal = case
+    announce(f"fa_bwd random {case}")
+    x = ai.prefill_inputs(seed, B, Hq, Hkv, Nq, d, dt, Nk=Nk)
+    do_bits = ai.grad_output(seed, B, Hq, Nq, d, dt)
+    dq, dk, dv = run_gpu(fa, x, do_bits, causal)
+    f = lambda a: ai.bits_to_f64(a, dt)
+    ref = oracle.attention_bwd(f(x["q"]), f(x["k"]), f(x["v"]), f(do_bits), 1.0 / math.sqrt(d), causal)
+    check_grads([from_dev(t, dt) for t in (dq, dk, dv)], ref, f"bwd random {case}")
+
+
 def test_bwd_deterministic(fa):
     """No atomics: two calls give the same bits."""
     import torch
