@@ -186,241 +186,242 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
   const int nb = (Nq + kBMs - 1) / kBMs;
   const int n_items = SPLIT && nb - 1 - wk.qt > wk.qt ? 2 : 1;
   for (int item = 0; item < n_items; ++item) {
-  const int q0 = SPLIT ? kBMs * (item == 0 ? nb - 1 - wk.qt : wk.qt) : wk.qt * kBM;
-  if (VARLEN && q0 >= Nq) return;  // past this sequence's rows (the whole workgroup)
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const int grp = wave >> 2;  // 0: matrix cores first; 1: softmax first
-  const int q0w = q0 + 32 * (SPLIT ? (wave & 3) : wave);  // first query row of this wave
-  const int off = Nk - Nq;         // causal: key j visible to query i iff j <= i + off
-  const int key0 = SPLIT ? grp * WR : 0;            // first key of a tile this wave multiplies
-  const uint32_t koff = (uint32_t)(key0 * 2 * D);  // its byte offset in a ring slot
+    const int q0 = SPLIT ? kBMs * (item == 0 ? nb - 1 - wk.qt : wk.qt) : wk.qt * kBM;
+    if (VARLEN && q0 >= Nq) return;  // past this sequence's rows (the whole workgroup)
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const int grp = wave >> 2;  // 0: matrix cores first; 1: softmax first
+    const int q0w = q0 + 32 * (SPLIT ? (wave & 3) : wave);  // first query row of this wave
+    const int off = Nk - Nq;         // causal: key j visible to query i iff j <= i + off
+    const int key0 = SPLIT ? grp * WR : 0;            // first key of a tile this wave multiplies
+    const uint32_t koff = (uint32_t)(key0 * 2 * D);  // its byte offset in a ring slot
 
-  const uint16_t* qp = sl.q;
-  const uint16_t* kp = sl.k;
-  const uint16_t* vp = sl.v;
+    const uint16_t* qp = sl.q;
+    const uint16_t* kp = sl.k;
+    const uint16_t* vp = sl.v;
 
-  // Key tiles this workgroup visits (none for rows that see no key).
-  int n_kv = (Nk + ROWS - 1) / ROWS;
-  if (CAUSAL) {
-    const int last_key = min(q0 + (SPLIT ? kBMs : kBM), Nq) - 1 + off;
-    n_kv = last_key < 0 ? 0 : min(n_kv, last_key / ROWS + 1);
-  }
-  // Key tiles this wave computes on (0 if the wave has no valid query row).
-  const bool wave_active = q0w < Nq;
-  int wave_tiles = wave_active ? n_kv : 0;
-  if (CAUSAL && wave_active) {
-    const int last = min(q0w + 31, Nq - 1) + off;
-    wave_tiles = last < key0 ? 0 : min(n_kv, (last - key0) / ROWS + 1);
-  }
-
-  // Q^T operand (B operand of S^T = K Q^T), held for the whole loop.
-  const int qrow = q0w + (lane & 31);
-  u32x4 qop[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (qrow < Nq)
-      qop[ks] = *reinterpret_cast<const u32x4*>(qp + (size_t)qrow * sl.qs + 16 * ks + 8 * half);
-    else
-      qop[ks] = u32x4{0u, 0u, 0u, 0u};
-  }
-  // Wait for Q here, once: the tile loads are asm the compiler does not count,
-  // so a Q wait it placed inside the loop would also wait for them.
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-
-  f32x16 acc_o[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc_o[mt][r] = 0.f;
-  float m_run = -__builtin_inff();  // row reference point, log2 units
-  float l_run = 0.f;                // this lane's share of the running sum
-  f32x16 s[KB];                     // S^T of the tile last multiplied
-  uint32_t pk[KB][8];               // P of the tile last softmaxed
-
-  // SM(j): mask the ragged key tail / causal diagonal, online softmax -> pk.
-  auto softmax = [&](int j) {
-    const int j0 = j * ROWS + key0;
-    const bool need_mask = (j0 + WR > Nk) || (CAUSAL && j0 + WR - 1 > q0w + off);
-    if (need_mask) {
-      const int lim = CAUSAL ? min(Nk, qrow + off + 1) : Nk;  // keys < lim are visible
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (j0 + 32 * kb + acc_key(r, half) >= lim) s[kb][r] = -__builtin_inff();
+    // Key tiles this workgroup visits (none for rows that see no key).
+    int n_kv = (Nk + ROWS - 1) / ROWS;
+    if (CAUSAL) {
+      const int last_key = min(q0 + (SPLIT ? kBMs : kBM), Nq) - 1 + off;
+      n_kv = last_key < 0 ? 0 : min(n_kv, last_key / ROWS + 1);
     }
-    softmax_step<DT, KB, MT>(s, scale_log2, m_run, l_run, acc_o, pk);
-  };
-  // Matrix-core phase: MB(jo) = O^T += V^T_jo P^T (if do_o), MA(js) = S^T = K_js Q^T (if do_s).
-  // mma_pre issues the first operand reads; mma finishes the phase.
-  u32x4 obuf[kPF];
-  auto mma_pre = [&](bool do_o, int jo, bool do_s, int js) {
-    const char* vl = vring + (jo % kSlots) * kTile + koff;
-    const char* kl = kring + (js % kSlots) * kTile + koff;
-    if (do_o && do_s)
-      mma_prefetch<D, WR, true, true, Rd>(obuf, vl, kl, lane);
-    else if (do_o)
-      mma_prefetch<D, WR, true, false, Rd>(obuf, vl, kl, lane);
-    else if (do_s)
-      mma_prefetch<D, WR, false, true, Rd>(obuf, vl, kl, lane);
-  };
-  auto mma = [&](bool do_o, int jo, bool do_s, int js) {
-    const char* vl = vring + (jo % kSlots) * kTile + koff;
-    const char* kl = kring + (js % kSlots) * kTile + koff;
-    if (do_o && do_s)
-      mma_run<DT, D, WR, true, true, Rd>(obuf, vl, kl, pk, qop, acc_o, s, lane);
-    else if (do_o)
-      mma_run<DT, D, WR, true, false, Rd>(obuf, vl, kl, pk, qop, acc_o, s, lane);
-    else if (do_s)
-      mma_run<DT, D, WR, false, true, Rd>(obuf, vl, kl, pk, qop, acc_o, s, lane);
-  };
-
-  // ---- direct-to-LDS tile loads, issued by the waves of group 0 only (they
-  // wait at the Y barrier anyway): 4 instructions per wave per tile.
-  const uint32_t lds_k = (uint32_t)(uintptr_t)(lds_void_t*)kring;
-  const uint32_t lds_v = (uint32_t)(uintptr_t)(lds_void_t*)vring;
-  const int wg = wv & 3;  // wave index within its group
-  const uint32_t ksb = 2u * (uint32_t)sl.ks, vsb = 2u * (uint32_t)sl.vs;  // row strides in bytes
-  const uint32_t dk = dma_src<D, false>(0, wg, lane, ROWS, ksb);  // source offsets of a full tile
-  const uint32_t dv = dma_src<D, true>(0, wg, lane, ROWS, vsb);
-  const long long kstep = (long long)RPI * sl.ks, vstep = (long long)RPI * sl.vs;
-  auto issue = [&](bool is_v, int t) {
-    const int nvalid = min(ROWS, Nk - t * ROWS);
-    const uint16_t* base = is_v ? vp + (long long)t * ROWS * sl.vs : kp + (long long)t * ROWS * sl.ks;
-    const uint32_t slot = (is_v ? lds_v : lds_k) + (uint32_t)((t % kSlots) * kTile) + (uint32_t)(64 * wg * 16);
-    if (nvalid == ROWS) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(base + (is_v ? vstep : kstep) * i, is_v ? dv : dk, slot + 4096 * i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dma16(base, is_v ? dma_src<D, true>(i, wg, lane, nvalid, vsb) : dma_src<D, false>(i, wg, lane, nvalid, ksb),
-              slot + 4096 * i);
+    // Key tiles this wave computes on (0 if the wave has no valid query row).
+    const bool wave_active = q0w < Nq;
+    int wave_tiles = wave_active ? n_kv : 0;
+    if (CAUSAL && wave_active) {
+      const int last = min(q0w + 31, Nq - 1) + off;
+      wave_tiles = last < key0 ? 0 : min(n_kv, (last - key0) / ROWS + 1);
     }
-  };
-  // Loads issued at the start of step i: K_{i+2} and V_{i+1}; returns the
-  // number of load instructions this thread issued (wave-uniform).
-  auto issue_step = [&](int i) -> int {
-    int n = 0;
-    if (grp == 0) {
-      if (i + 2 < n_kv) {
-        issue(false, i + 2);
-        n += 4;
+
+    // Q^T operand (B operand of S^T = K Q^T), held for the whole loop.
+    const int qrow = q0w + (lane & 31);
+    u32x4 qop[KS];
+  #pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (qrow < Nq)
+        qop[ks] = *reinterpret_cast<const u32x4*>(qp + (size_t)qrow * sl.qs + 16 * ks + 8 * half);
+      else
+        qop[ks] = u32x4{0u, 0u, 0u, 0u};
+    }
+    // Wait for Q here, once: the tile loads are asm the compiler does not count,
+    // so a Q wait it placed inside the loop would also wait for them.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+    f32x16 acc_o[MT];
+  #pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[mt][r] = 0.f;
+    float m_run = -__builtin_inff();  // row reference point, log2 units
+    float l_run = 0.f;                // this lane's share of the running sum
+    f32x16 s[KB];                     // S^T of the tile last multiplied
+    uint32_t pk[KB][8];               // P of the tile last softmaxed
+
+    // SM(j): mask the ragged key tail / causal diagonal, online softmax -> pk.
+    auto softmax = [&](int j) {
+      const int j0 = j * ROWS + key0;
+      const bool need_mask = (j0 + WR > Nk) || (CAUSAL && j0 + WR - 1 > q0w + off);
+      if (need_mask) {
+        const int lim = CAUSAL ? min(Nk, qrow + off + 1) : Nk;  // keys < lim are visible
+  #pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (j0 + 32 * kb + acc_key(r, half) >= lim) s[kb][r] = -__builtin_inff();
       }
-      if (i + 1 < n_kv) {
-        issue(true, i + 1);
-        n += 4;
-      }
-    }
-    return n;
-  };
+      softmax_step<DT, KB, MT>(s, scale_log2, m_run, l_run, acc_o, pk);
+    };
+    // Matrix-core phase: MB(jo) = O^T += V^T_jo P^T (if do_o), MA(js) = S^T = K_js Q^T (if do_s).
+    // mma_pre issues the first operand reads; mma finishes the phase.
+    u32x4 obuf[kPF];
+    auto mma_pre = [&](bool do_o, int jo, bool do_s, int js) {
+      const char* vl = vring + (jo % kSlots) * kTile + koff;
+      const char* kl = kring + (js % kSlots) * kTile + koff;
+      if (do_o && do_s)
+        mma_prefetch<D, WR, true, true, Rd>(obuf, vl, kl, lane);
+      else if (do_o)
+        mma_prefetch<D, WR, true, false, Rd>(obuf, vl, kl, lane);
+      else if (do_s)
+        mma_prefetch<D, WR, false, true, Rd>(obuf, vl, kl, lane);
+    };
+    auto mma = [&](bool do_o, int jo, bool do_s, int js) {
+      const char* vl = vring + (jo % kSlots) * kTile + koff;
+      const char* kl = kring + (js % kSlots) * kTile + koff;
+      if (do_o && do_s)
+        mma_run<DT, D, WR, true, true, Rd>(obuf, vl, kl, pk, qop, acc_o, s, lane);
+      else if (do_o)
+        mma_run<DT, D, WR, true, false, Rd>(obuf, vl, kl, pk, qop, acc_o, s, lane);
+      else if (do_s)
+        mma_run<DT, D, WR, false, true, Rd>(obuf, vl, kl, pk, qop, acc_o, s, lane);
+    };
 
-  // Prologue: K_0 (read first), then K_1 and V_0 (the loads of "step -1").
-  if (grp == 0 && 0 < n_kv) issue(false, 0);
-  dma_barrier(issue_step(-1));  // K_0 has landed
-
-  // Step i = phase A, barrier Y_i, phase B; Y_i is the step's only barrier:
-  //   group 0: A = MB(i-1), MA(i), loads K_{i+2}, V_{i+1}   B = SM(i), first reads of MB(i), MA(i+1)
-  //   group 1: A = SM(i-1), first reads of MB(i-1), MA(i)  B = MB(i-1), MA(i)
-  // Y_i waits for the loads issued in step i - 1 (K_{i+1}, V_i). Between Y_i
-  // and Y_{i+1} the waves read K_i, K_{i+1}, V_{i-1} and V_i, while the loads
-  // in flight write K_{i+2}, K_{i+3}, V_{i+1} and V_{i+2}: distinct slots of
-  // the 4-slot rings. A slot is rewritten only after the barrier that follows
-  // the MFMAs consuming its last reads.
-  if (grp == 0) {
-    mma_pre(false, 0, 0 < wave_tiles, 0);
-    for (int i = 0; i <= n_kv; ++i) {
-      const bool do_o = i >= 1 && i - 1 < wave_tiles, do_s = i < wave_tiles;
-      const bool has_k = i + 2 < n_kv, has_v = i + 1 < n_kv;
-      const int n_new = 4 * has_k + 4 * has_v;
-      if (do_o && do_s) {
-        // full phase: with full tiles the loads are spread over its MFMAs
-        const bool spread = (!has_k || Nk - (i + 2) * ROWS >= ROWS) && (!has_v || Nk - (i + 1) * ROWS >= ROWS);
-        if (!spread) issue_step(i);
-        const DmaSpread<MmaPlan<D, WR, true, true, Rd>::N> ex{kp + (long long)(i + 2) * ROWS * sl.ks, vp + (long long)(i + 1) * ROWS * sl.vs,
-                           lds_k + (uint32_t)(((i + 2) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
-                           lds_v + (uint32_t)(((i + 1) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
-                           has_k && spread, has_v && spread, dk, dv, kstep, vstep};
-        mma_run<DT, D, WR, true, true, Rd>(obuf, vring + ((i - 1) % kSlots) * kTile + koff,
-                                                  kring + (i % kSlots) * kTile + koff, pk, qop, acc_o, s, lane, ex);
+    // ---- direct-to-LDS tile loads, issued by the waves of group 0 only (they
+    // wait at the Y barrier anyway): 4 instructions per wave per tile.
+    const uint32_t lds_k = (uint32_t)(uintptr_t)(lds_void_t*)kring;
+    const uint32_t lds_v = (uint32_t)(uintptr_t)(lds_void_t*)vring;
+    const int wg = wv & 3;  // wave index within its group
+    const uint32_t ksb = 2u * (uint32_t)sl.ks, vsb = 2u * (uint32_t)sl.vs;  // row strides in bytes
+    const uint32_t dk = dma_src<D, false>(0, wg, lane, ROWS, ksb);  // source offsets of a full tile
+    const uint32_t dv = dma_src<D, true>(0, wg, lane, ROWS, vsb);
+    const long long kstep = (long long)RPI * sl.ks, vstep = (long long)RPI * sl.vs;
+    auto issue = [&](bool is_v, int t) {
+      const int nvalid = min(ROWS, Nk - t * ROWS);
+      const uint16_t* base = is_v ? vp + (long long)t * ROWS * sl.vs : kp + (long long)t * ROWS * sl.ks;
+      const uint32_t slot = (is_v ? lds_v : lds_k) + (uint32_t)((t % kSlots) * kTile) + (uint32_t)(64 * wg * 16);
+      if (nvalid == ROWS) {
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) dma16(base + (is_v ? vstep : kstep) * i, is_v ? dv : dk, slot + 4096 * i);
       } else {
-        issue_step(i);
-        if (do_o)
-          mma_run<DT, D, WR, true, false, Rd>(obuf, vring + ((i - 1) % kSlots) * kTile + koff,
-                                                     kring + (i % kSlots) * kTile + koff, pk, qop, acc_o, s, lane);
-        else if (do_s)
-          mma_run<DT, D, WR, false, true, Rd>(obuf, vring + koff, kring + (i % kSlots) * kTile + koff, pk, qop,
-                                                     acc_o, s, lane);
+  #pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dma16(base, is_v ? dma_src<D, true>(i, wg, lane, nvalid, vsb) : dma_src<D, false>(i, wg, lane, nvalid, ksb),
+                slot + 4096 * i);
       }
-      dma_barrier(n_new);  // Y_i
-      if (i < wave_tiles) softmax(i);
-      mma_pre(i < wave_tiles, i, i + 1 < wave_tiles, i + 1);
-    }
-  } else {
-    for (int i = 0; i <= n_kv; ++i) {
-      const int n_new = issue_step(i);
-      if (i >= 1 && i - 1 < wave_tiles) softmax(i - 1);
-      mma_pre(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
-      dma_barrier(n_new);  // Y_i
-      mma(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
-    }
-  }
-
-  // ---- epilogue: normalise once, write O and LSE
-  auto epilogue = [&]() {
-    const float l_tot = halves_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qrow < Nq) {
-      uint16_t* orow = sl.o + (size_t)qrow * sl.os;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d0 = 32 * mt + 8 * i + 4 * half;
-          const u32x2 w = {pack2<DT>(acc_o[mt][4 * i] * inv, acc_o[mt][4 * i + 1] * inv),
-                           pack2<DT>(acc_o[mt][4 * i + 2] * inv, acc_o[mt][4 * i + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + d0) = w;
+    };
+    // Loads issued at the start of step i: K_{i+2} and V_{i+1}; returns the
+    // number of load instructions this thread issued (wave-uniform).
+    auto issue_step = [&](int i) -> int {
+      int n = 0;
+      if (grp == 0) {
+        if (i + 2 < n_kv) {
+          issue(false, i + 2);
+          n += 4;
         }
-      if (sl.lse != nullptr && half == 0)
-        sl.lse[qrow] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
-    }
-  };
-  if constexpr (!SPLIT) {
-    if (!wave_active) return;
-    epilogue();
-  } else {
-    // Join the two key halves of each row. Group 1 leaves its (m, l, O^T
-    // accumulator) in LDS, in the ring whose last reads the first barrier
-    // orders; group 0 merges them into its own and writes the block. The
-    // third barrier keeps the next block's loads off the buffer until then.
-    constexpr int XW = 16 * MT + 2;  // floats per lane
-    float* const xb = reinterpret_cast<float*>(smem) + (wave & 3) * (XW * 64) + lane;
-    __syncthreads();
-    if (grp == 1) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) xb[(16 * mt + r) * 64] = acc_o[mt][r];
-      xb[16 * MT * 64] = m_run;
-      xb[(16 * MT + 1) * 64] = l_run;
-    }
-    __syncthreads();
+        if (i + 1 < n_kv) {
+          issue(true, i + 1);
+          n += 4;
+        }
+      }
+      return n;
+    };
+
+    // Prologue: K_0 (read first), then K_1 and V_0 (the loads of "step -1").
+    if (grp == 0 && 0 < n_kv) issue(false, 0);
+    dma_barrier(issue_step(-1));  // K_0 has landed
+
+    // Step i = phase A, barrier Y_i, phase B; Y_i is the step's only barrier:
+    //   group 0: A = MB(i-1), MA(i), loads K_{i+2}, V_{i+1}   B = SM(i), first reads of MB(i), MA(i+1)
+    //   group 1: A = SM(i-1), first reads of MB(i-1), MA(i)  B = MB(i-1), MA(i)
+    // Y_i waits for the loads issued in step i - 1 (K_{i+1}, V_i). Between Y_i
+    // and Y_{i+1} the waves read K_i, K_{i+1}, V_{i-1} and V_i, while the loads
+    // in flight write K_{i+2}, K_{i+3}, V_{i+1} and V_{i+2}: distinct slots of
+    // the 4-slot rings. A slot is rewritten only after the barrier that follows
+    // the MFMAs consuming its last reads.
     if (grp == 0) {
-      const float m1 = xb[16 * MT * 64], l1 = xb[(16 * MT + 1) * 64];
-      const float m = fmaxf(m_run, m1);
-      const float a0 = m_run == -__builtin_inff() ? 0.f : exp2_fast(m_run - m);
-      const float a1 = m1 == -__builtin_inff() ? 0.f : exp2_fast(m1 - m);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[mt][r] = a0 * acc_o[mt][r] + a1 * xb[(16 * mt + r) * 64];
-      l_run = a0 * l_run + a1 * l1;
-      m_run = m;
-      if (wave_active) epilogue();
+      mma_pre(false, 0, 0 < wave_tiles, 0);
+      for (int i = 0; i <= n_kv; ++i) {
+        const bool do_o = i >= 1 && i - 1 < wave_tiles, do_s = i < wave_tiles;
+        const bool has_k = i + 2 < n_kv, has_v = i + 1 < n_kv;
+        const int n_new = 4 * has_k + 4 * has_v;
+        if (do_o && do_s) {
+          // full phase: with full tiles the loads are spread over its MFMAs
+          const bool spread = (!has_k || Nk - (i + 2) * ROWS >= ROWS) && (!has_v || Nk - (i + 1) * ROWS >= ROWS);
+          if (!spread) issue_step(i);
+          const DmaSpread<MmaPlan<D, WR, true, true, Rd>::N> ex{kp + (long long)(i + 2) * ROWS * sl.ks,
+                                                              vp + (long long)(i + 1) * ROWS * sl.vs,
+                             lds_k + (uint32_t)(((i + 2) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
+                             lds_v + (uint32_t)(((i + 1) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
+                             has_k && spread, has_v && spread, dk, dv, kstep, vstep};
+          mma_run<DT, D, WR, true, true, Rd>(obuf, vring + ((i - 1) % kSlots) * kTile + koff,
+                                                    kring + (i % kSlots) * kTile + koff, pk, qop, acc_o, s, lane, ex);
+        } else {
+          issue_step(i);
+          if (do_o)
+            mma_run<DT, D, WR, true, false, Rd>(obuf, vring + ((i - 1) % kSlots) * kTile + koff,
+                                                       kring + (i % kSlots) * kTile + koff, pk, qop, acc_o, s, lane);
+          else if (do_s)
+            mma_run<DT, D, WR, false, true, Rd>(obuf, vring + koff, kring + (i % kSlots) * kTile + koff, pk, qop,
+                                                       acc_o, s, lane);
+        }
+        dma_barrier(n_new);  // Y_i
+        if (i < wave_tiles) softmax(i);
+        mma_pre(i < wave_tiles, i, i + 1 < wave_tiles, i + 1);
+      }
+    } else {
+      for (int i = 0; i <= n_kv; ++i) {
+        const int n_new = issue_step(i);
+        if (i >= 1 && i - 1 < wave_tiles) softmax(i - 1);
+        mma_pre(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
+        dma_barrier(n_new);  // Y_i
+        mma(i >= 1 && i - 1 < wave_tiles, i - 1, i < wave_tiles, i);
+      }
     }
-    __syncthreads();
-  }
+
+    // ---- epilogue: normalise once, write O and LSE
+    auto epilogue = [&]() {
+      const float l_tot = halves_sum(l_run);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      if (qrow < Nq) {
+        uint16_t* orow = sl.o + (size_t)qrow * sl.os;
+  #pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d0 = 32 * mt + 8 * i + 4 * half;
+            const u32x2 w = {pack2<DT>(acc_o[mt][4 * i] * inv, acc_o[mt][4 * i + 1] * inv),
+                             pack2<DT>(acc_o[mt][4 * i + 2] * inv, acc_o[mt][4 * i + 3] * inv)};
+            *reinterpret_cast<u32x2*>(orow + d0) = w;
+          }
+        if (sl.lse != nullptr && half == 0)
+          sl.lse[qrow] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
+      }
+    };
+    if constexpr (!SPLIT) {
+      if (!wave_active) return;
+      epilogue();
+    } else {
+      // Join the two key halves of each row. Group 1 leaves its (m, l, O^T
+      // accumulator) in LDS, in the ring whose last reads the first barrier
+      // orders; group 0 merges them into its own and writes the block. The
+      // third barrier keeps the next block's loads off the buffer until then.
+      constexpr int XW = 16 * MT + 2;  // floats per lane
+      float* const xb = reinterpret_cast<float*>(smem) + (wave & 3) * (XW * 64) + lane;
+      __syncthreads();
+      if (grp == 1) {
+  #pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) xb[(16 * mt + r) * 64] = acc_o[mt][r];
+        xb[16 * MT * 64] = m_run;
+        xb[(16 * MT + 1) * 64] = l_run;
+      }
+      __syncthreads();
+      if (grp == 0) {
+        const float m1 = xb[16 * MT * 64], l1 = xb[(16 * MT + 1) * 64];
+        const float m = fmaxf(m_run, m1);
+        const float a0 = m_run == -__builtin_inff() ? 0.f : exp2_fast(m_run - m);
+        const float a1 = m1 == -__builtin_inff() ? 0.f : exp2_fast(m1 - m);
+  #pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[mt][r] = a0 * acc_o[mt][r] + a1 * xb[(16 * mt + r) * 64];
+        l_run = a0 * l_run + a1 * l1;
+        m_run = m;
+        if (wave_active) epilogue();
+      }
+      __syncthreads();
+    }
   }  // item
 }
 
