@@ -63,59 +63,6 @@ __device__ inline int chunk_pos(int row, int c) {
   else return c ^ ((4 * (((row >> 1) & 1) ^ (a & 1)) + a) & 7);
 }
 
-// Row operand (A of a rows x d product): row `row`, 8 elements from chunk c.
-template <int D>
-__device__ inline u32x4 row_op(const char* __restrict__ t, int row, int c) {
-  return *reinterpret_cast<const u32x4*>(t + row * (D * 2) + chunk_pos<D>(row, c) * 16);
-}
-
-// Transposed operand (A of a d x rows product): lane l receives
-// T[16 G + 8 p + 4 h + e][32 mt + l % 32] for e = 0..3, p = 0, 1 (h = l / 32),
-// the row order in which an accumulator holds its rows (acc_key), so a
-// packed accumulator is the matching B operand.
-template <int D>
-__device__ inline u32x4 tr_op(const char* __restrict__ t, int G, int mt, int lane) {
-  const int gi = lane >> 4, e = (lane >> 2) & 3, qq = lane & 3;
-  const int h = gi >> 1, dh = gi & 1;
-  const int c = 4 * mt + 2 * dh + (qq >> 1);
-  u32x4 out;
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int row = 16 * G + 8 * p + 4 * h + e;
-    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4_t*)(t + row * (D * 2) + chunk_pos<D>(row, c) * 16 + 8 * (qq & 1)));
-    const u32x2 w = __builtin_bit_cast(u32x2, x);
-    out[2 * p] = w[0];
-    out[2 * p + 1] = w[1];
-  }
-  return out;
-}
-
-// Global -> registers -> LDS staging of one [64][D] tile by 256 threads:
-// NP 16-byte chunks per thread, rows at or beyond nvalid re-read row
-// nvalid - 1 (their contributions are masked to zero).
-template <int D>
-struct Stage {
-  static constexpr int CPR = D / 8;
-  static constexpr int NP = kTileRows * CPR / kThreads;
-  __device__ static inline void load(const uint16_t* __restrict__ base, int nvalid, u32x4 (&r)[NP]) {
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int idx = threadIdx.x + kThreads * p;
-      const int row = min(idx / CPR, nvalid - 1), c = idx % CPR;
-      r[p] = *reinterpret_cast<const u32x4*>(base + (size_t)row * D + c * 8);
-    }
-  }
-  __device__ static inline void store(char* __restrict__ t, const u32x4 (&r)[NP]) {
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int idx = threadIdx.x + kThreads * p;
-      const int row = idx / CPR, c = idx % CPR;
-      *reinterpret_cast<u32x4*>(t + row * (D * 2) + chunk_pos<D>(row, c) * 16) = r[p];
-    }
-  }
-};
-
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // One 1 KiB direct-to-LDS load: lane l's 16 bytes from sbase + voff land at
@@ -297,8 +244,11 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
 
   // Lane offsets (bytes in a [64][D] tile) of the operand reads: the row
   // operand (row 32 RH + lane % 32, chunk 2 ks + half) and the transposed
-  // operand of 16-row group 0 (tr_op's pattern); group G adds 16 G rows,
-  // since the swizzle depends on the row only through row % 16.
+  // one (two ds_read_b64_tr_b16: lane l receives T[16 G + 8 p + 4 h + e]
+  // [32 mt + l % 32] for e = 0..3, p = 0, 1, h = l / 32, the row order of an
+  // accumulator, so a packed accumulator is the matching B operand) for
+  // 16-row group G = 0; group G adds 16 G rows, since the swizzle depends on
+  // the row only through row % 16.
   auto row_off = [&](int rh_, int ks) {
     const int row = 32 * rh_ + (lane & 31);
     return (uint32_t)(row * (D * 2) + chunk_pos<D>(row, 2 * ks + half) * 16);
@@ -586,9 +536,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(
   };
 
   // Lane offsets (bytes in a [64][D] tile) of the operand reads: K or V rows
-  // lane % 32 (+ 32 kb, a constant), chunk 2 ks + half; K^T transposed as
-  // tr_op reads it for 16-row group 0 (group G adds 16 G rows, since the
-  // swizzle depends on the row only through row % 16).
+  // lane % 32 (+ 32 kb, a constant), chunk 2 ks + half; K^T transposed (the
+  // pattern of the dK/dV kernel) for 16-row group 0, group G adding 16 G
+  // rows, since the swizzle depends on the row only through row % 16.
   uint32_t rwo[KS], tro[MT][2];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
