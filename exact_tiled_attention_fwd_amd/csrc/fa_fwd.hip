@@ -166,7 +166,8 @@ struct DmaSpread {
 // query rows and the two groups take the two halves of every key tile; at
 // the end of a block the halves are joined by the merge identity of "The
 // math of Flash Attention" through LDS. Tiles, ring and loads are those of
-// the 256-row mode.
+// the 256-row mode; the second block's Q and first K and V tiles are loaded
+// while the first is joined and written.
 template <int DT, int D, bool CAUSAL, bool VARLEN, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -176,7 +177,14 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
   constexpr int WR = SPLIT ? ROWS / 2 : ROWS;  // keys of a tile one wave multiplies
   constexpr int KS = D / 16, KB = WR / 32, MT = D / 32;
   using Rd = DmaReader<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kSlots * kTile];
+  // Split mode joins the key halves through LDS from V slot 1 on (16 MT + 2
+  // floats per lane), so that K slots 0, 1 and V slot 0 can take the next
+  // block's first tiles meanwhile.
+  constexpr int XW = 16 * MT + 2;
+  constexpr int kXOff = (kSlots + 1) * kTile;
+  constexpr int kSmem = SPLIT && kXOff + 4 * XW * 64 * 4 > 2 * kSlots * kTile ? kXOff + 4 * XW * 64 * 4
+                                                                             : 2 * kSlots * kTile;
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
   char* const kring = smem;                   // K tile t in slot t % 4
   char* const vring = smem + kSlots * kTile;  // V tile t in slot t % 4
 
@@ -185,18 +193,32 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
   const int Nq = sl.Nq, Nk = sl.Nk;
   const int nb = (Nq + kBMs - 1) / kBMs;
   const int n_items = SPLIT && nb - 1 - wk.qt > wk.qt ? 2 : 1;
+  u32x4 qop[KS];  // Q^T operand (B operand of S^T = K Q^T), held for a whole block
   for (int item = 0; item < n_items; ++item) {
-    const int q0 = SPLIT ? kBMs * (item == 0 ? nb - 1 - wk.qt : wk.qt) : wk.qt * kBM;
-    if (VARLEN && q0 >= Nq) return;  // past this sequence's rows (the whole workgroup)
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int grp = wave >> 2;  // 0: matrix cores first; 1: softmax first
+    // Q^T of the rows from q0x on
+    auto load_q = [&](int q0x) {
+      const int qr = q0x + 32 * (SPLIT ? (wave & 3) : wave) + (lane & 31);
+  #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (qr < Nq)
+          qop[ks] = *reinterpret_cast<const u32x4*>(sl.q + (size_t)qr * sl.qs + 16 * ks + 8 * half);
+        else
+          qop[ks] = u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    const int q0 = SPLIT ? kBMs * (item == 0 ? nb - 1 - wk.qt : wk.qt) : wk.qt * kBM;
+    if (VARLEN && q0 >= Nq) return;  // past this sequence's rows (the whole workgroup)
+    // The second block of split mode has its Q and first tiles in flight
+    // since the end of the first.
+    const bool prefetched = SPLIT && item > 0;
     const int q0w = q0 + 32 * (SPLIT ? (wave & 3) : wave);  // first query row of this wave
     const int off = Nk - Nq;         // causal: key j visible to query i iff j <= i + off
     const int key0 = SPLIT ? grp * WR : 0;            // first key of a tile this wave multiplies
     const uint32_t koff = (uint32_t)(key0 * 2 * D);  // its byte offset in a ring slot
 
-    const uint16_t* qp = sl.q;
     const uint16_t* kp = sl.k;
     const uint16_t* vp = sl.v;
 
@@ -214,16 +236,8 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
       wave_tiles = last < key0 ? 0 : min(n_kv, (last - key0) / ROWS + 1);
     }
 
-    // Q^T operand (B operand of S^T = K Q^T), held for the whole loop.
     const int qrow = q0w + (lane & 31);
-    u32x4 qop[KS];
-  #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (qrow < Nq)
-        qop[ks] = *reinterpret_cast<const u32x4*>(qp + (size_t)qrow * sl.qs + 16 * ks + 8 * half);
-      else
-        qop[ks] = u32x4{0u, 0u, 0u, 0u};
-    }
+    if (!prefetched) load_q(q0);
     // Wait for Q here, once: the tile loads are asm the compiler does not count,
     // so a Q wait it placed inside the loop would also wait for them.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -317,8 +331,12 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
     };
 
     // Prologue: K_0 (read first), then K_1 and V_0 (the loads of "step -1").
-    if (grp == 0 && 0 < n_kv) issue(false, 0);
-    dma_barrier(issue_step(-1));  // K_0 has landed
+    if (prefetched) {
+      dma_barrier(0);  // K_0, K_1, V_0 (waited for with Q above)
+    } else {
+      if (grp == 0 && 0 < n_kv) issue(false, 0);
+      dma_barrier(issue_step(-1));  // K_0 has landed
+    }
 
     // Step i = phase A, barrier Y_i, phase B; Y_i is the step's only barrier:
     //   group 0: A = MB(i-1), MA(i), loads K_{i+2}, V_{i+1}   B = SM(i), first reads of MB(i), MA(i+1)
@@ -368,6 +386,25 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
       }
     }
 
+    // Split mode, first block: every wave is past the last barrier, so no K
+    // slot is read any more, and group 1 has finished its last V reads (group
+    // 0 finished them before that barrier). Load the next block's K_0, K_1
+    // (group 0) and V_0 (group 1) now, and its Q (group 1 here, group 0 once
+    // its join is done); the buffer of the join starts at V slot 1.
+    const bool next = SPLIT && item + 1 < n_items;
+    const int q0n = kBMs * wk.qt;
+    if (next) {
+      const int last_key = min(q0n + kBMs, Nq) - 1 + off;
+      const int n_kvn = last_key < 0 ? 0 : min((Nk + ROWS - 1) / ROWS, last_key / ROWS + 1);
+      if (grp == 0) {
+        if (0 < n_kvn) issue(false, 0);
+        if (1 < n_kvn) issue(false, 1);
+      } else {
+        if (0 < n_kvn) issue(true, 0);
+        load_q(q0n);
+      }
+    }
+
     // ---- epilogue: normalise once, write O and LSE
     auto epilogue = [&]() {
       const float l_tot = halves_sum(l_run);
@@ -392,11 +429,11 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
       epilogue();
     } else {
       // Join the two key halves of each row. Group 1 leaves its (m, l, O^T
-      // accumulator) in LDS, in the ring whose last reads the first barrier
-      // orders; group 0 merges them into its own and writes the block. The
-      // third barrier keeps the next block's loads off the buffer until then.
-      constexpr int XW = 16 * MT + 2;  // floats per lane
-      float* const xb = reinterpret_cast<float*>(smem) + (wave & 3) * (XW * 64) + lane;
+      // accumulator) in LDS from V slot 1 on, past the first barrier (its own
+      // last V reads); group 0 merges them into its own and writes the block.
+      // The third barrier keeps the next block's loads (V_1 at its first
+      // step) off the buffer until then.
+      float* const xb = reinterpret_cast<float*>(smem + kXOff) + (wave & 3) * (XW * 64) + lane;
       __syncthreads();
       if (grp == 1) {
   #pragma unroll
@@ -418,6 +455,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
           for (int r = 0; r < 16; ++r) acc_o[mt][r] = a0 * acc_o[mt][r] + a1 * xb[(16 * mt + r) * 64];
         l_run = a0 * l_run + a1 * l1;
         m_run = m;
+        if (next) load_q(q0n);
         if (wave_active) epilogue();
       }
       __syncthreads();
