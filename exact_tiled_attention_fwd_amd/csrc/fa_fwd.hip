@@ -174,6 +174,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
     uint16_t* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Nq_all, int Nk_all,
     float scale_log2, int n_qt, Varlen vlen, Layout ly) {
   constexpr int ROWS = Geo<D>::ROWS, kTile = Geo<D>::TILE, RPI = Geo<D>::RPI;
+  static_assert(!SPLIT || (CAUSAL && !VARLEN), "split mode serves causal, unpacked grids");
   constexpr int WR = SPLIT ? ROWS / 2 : ROWS;  // keys of a tile one wave multiplies
   constexpr int KS = D / 16, KB = WR / 32, MT = D / 32;
   using Rd = DmaReader<D>;
