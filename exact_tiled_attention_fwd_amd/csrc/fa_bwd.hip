@@ -97,6 +97,8 @@ __device__ inline float lse2_of(const float* __restrict__ lse, int row, int n) {
   const float x = lse[row];
   return x > -__builtin_inff() ? x * kLog2e : __builtin_inff();
 }
+// The same for an LSE value already loaded.
+__device__ inline float lse2_of_value(float x) { return x > -__builtin_inff() ? x * kLog2e : __builtin_inff(); }
 
 // The two 16-bit values packed in w (low half first) as fp32, exactly.
 template <int DT>
@@ -233,13 +235,20 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
 #pragma unroll
       for (int i = 0; i < TILE / 8192; ++i) dma16(base, dma_off8<D>(i, wv, lane, nvalid), dst + 8192 * i);
     }
-    if (threadIdx.x < kTileRows)
-      rl = lse2_of(lse + qo + i0, threadIdx.x, Nq - i0);
-    else if (threadIdx.x < 2 * kTileRows)
-      rl = (i0 + (int)threadIdx.x - kTileRows < Nq) ? delta[qo + i0 + threadIdx.x - kTileRows] : 0.f;
+    // One plain load per thread of 0..127 (LSE, then delta), of a row that
+    // exists; nothing is computed from it until put_rl, so no wait for it
+    // (or for the tile loads before it) is placed here.
+    if (threadIdx.x < 2 * kTileRows) {
+      const int r = (int)threadIdx.x % kTileRows;
+      rl = (threadIdx.x < kTileRows ? lse : delta)[qo + i0 + min(r, Nq - i0 - 1)];
+    }
   };
-  auto put_rl = [&](int slot) {
-    if (threadIdx.x < 2 * kTileRows) reinterpret_cast<float*>(smem + slot * BUF + 2 * TILE)[threadIdx.x] = rl;
+  auto put_rl = [&](int slot, int i0) {  // i0: first row of the tile in that slot
+    if (threadIdx.x < 2 * kTileRows) {
+      const bool row_ok = (int)threadIdx.x % kTileRows < Nq - i0;
+      const float x = threadIdx.x < kTileRows ? (row_ok ? lse2_of_value(rl) : __builtin_inff()) : (row_ok ? rl : 0.f);
+      reinterpret_cast<float*>(smem + slot * BUF + 2 * TILE)[threadIdx.x] = x;
+    }
   };
 
   // Lane offsets (bytes in a [64][D] tile) of the operand reads: the row
@@ -435,7 +444,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
       for (int q2 = 0; q2 < 8; ++q2) own[q2] = fresh[q2];
       p_own = a_own;
       p_oth = a_oth;
-      if (it + 1 < total) put_rl(nxt);
+      if (it + 1 < total) put_rl(nxt, tile_at(ti_n) * kTileRows);
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile it + 1 has landed
       __syncthreads();
       prv = cur;
@@ -448,7 +457,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
 
   if (total > 0) {
     issue(tile_at(0), 0, 0);
-    put_rl(0);
+    put_rl(0, tile_at(0) * kTileRows);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
