@@ -497,7 +497,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_bwd_dq_kernel(
   const Work wk = map_work(blockIdx.x, B, Hq, Hkv, n_qt);
   const int qt = wk.qt, b = wk.b, h = wk.h, g = wk.g;
   const int bh = b * Hq + h;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, half = lane >> 5;
+  // wave index read as wave-uniform, so that the per-tile mask test below is
+  // a scalar branch (tiles off the diagonal skip the masking entirely)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, half = lane >> 5;
   const int q0 = qt * kBwdQueryRows;
   const int q0w = q0 + 32 * wave;                  // first query row of this wave
   const int qrow = q0w + (lane & 31);             // this lane's query column
