@@ -351,8 +351,20 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
       const float* l2 = reinterpret_cast<const float*>(tile + 2 * TILE);
       const float* dl = l2 + kTileRows;
       const int r0 = i0 + 32 * RH;
-      const bool need_mask = (wk0 + 31 >= Nk) || (CAUSAL && wk0 + 31 > r0 + off);
+      // the same in every lane; read as wave-uniform so that tiles off the
+      // diagonal skip the masking by a scalar branch
+      const bool need_mask =
+          __builtin_amdgcn_readfirstlane((int)((wk0 + 31 >= Nk) || (CAUSAL && wk0 + 31 > r0 + off))) != 0;
       uint32_t pk[8], dsk[8];
+      // masked scores to -inf first (their P and dS are then exactly 0), so
+      // the exponentials below carry no per-element select
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i0 + 32 * RH + 8 * (r >> 2) + 4 * half + (r & 3);
+          if ((key >= Nk) | (CAUSAL & (key > row + off))) s[r] = -__builtin_inff();
+        }
+      }
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int rl0 = 32 * RH + 8 * m + 4 * half;
@@ -362,11 +374,7 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * m + e;
-          float x = exp2_fast(__builtin_fmaf(s[r], c2, -L[e]));
-          if (need_mask) {
-            const bool hide = (key >= Nk) | (CAUSAL & (key > i0 + rl0 + e + off));
-            x = hide ? 0.f : x;
-          }
+          const float x = exp2_fast(__builtin_fmaf(s[r], c2, -L[e]));
           p[e] = x;
           ds[e] = x * (dp[r] - Dv[e]);
         }
