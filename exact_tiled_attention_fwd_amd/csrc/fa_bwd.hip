@@ -145,14 +145,6 @@ __global__ __launch_bounds__(kThreads) void fa_bwd_delta_kernel(const uint16_t* 
 // registers as the B operands of S and dP.
 constexpr int kDkdvThreads = 512;
 
-template <int D>
-__device__ inline uint32_t dma_off8(int i, int w, int lane, int nvalid) {  // 8 loading waves
-  constexpr int CPR = D / 8;
-  const int p = 512 * i + 64 * w + lane;
-  const int row = p / CPR, pos = p % CPR;
-  return (uint32_t)(min(row, nvalid - 1) * (D * 2) + chunk_pos<D>(row, pos) * 16);
-}
-
 template <bool V>
 struct BoolC {
   static constexpr bool value = V;
@@ -228,12 +220,16 @@ __global__ __launch_bounds__(kDkdvThreads, 1) void fa_bwd_dkdv_kernel(
     const size_t qo = ((size_t)b * Hq + h) * Nq;
     const int i0 = t * kTileRows;
     const int nvalid = min(kTileRows, Nq - i0);
+    // the Q and dO loads come from the dV waves only (a quarter of each
+    // tile per wave): the dK waves' path through a tile is the longer one
+    if (dv_wave) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint16_t* base = (u ? dout : q) + (qo + i0) * D;
-      const uint32_t dst = lds0 + (uint32_t)(slot * BUF + u * TILE + 64 * wv * 16);
+      for (int u = 0; u < 2; ++u) {
+        const uint16_t* base = (u ? dout : q) + (qo + i0) * D;
+        const uint32_t dst = lds0 + (uint32_t)(slot * BUF + u * TILE + 64 * wv * 16);
 #pragma unroll
-      for (int i = 0; i < TILE / 8192; ++i) dma16(base, dma_off8<D>(i, wv, lane, nvalid), dst + 8192 * i);
+        for (int i = 0; i < TILE / 4096; ++i) dma16(base, dma_off<D>(i, wv, lane, nvalid), dst + 4096 * i);
+      }
     }
     // One plain load per thread of 0..127 (LSE, then delta), of a row that
     // exists; nothing is computed from it until put_rl, so no wait for it
