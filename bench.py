@@ -8,7 +8,9 @@ One step = one pass of the whole path over one batch of synthetic input:
     Hkv=8, d=128, bf16, cache lengths uniform in [1024, 32768].
 Inputs are generated once, copied to HBM, and stay resident; the timed region
 holds only the library calls. Each call is bracketed by HIP events on the
-stream it is launched on.
+stream it is launched on. Before the W warmup steps, untimed steps run back to
+back for --settle seconds (0.5 by default) so that the GPU has left its idle
+clocks; the K timed steps are then exactly K passes of the whole path.
 
 Prints ONE JSON line on stdout. `value` is prefill TFLOP/s counting
 4*B*Hq*Nq*Nk*d FLOPs halved for causal; `decode` carries decode GB/s counting
@@ -306,6 +308,27 @@ class DecodePaged(Decode):
                              workspace=self.ws, out=self.o, lse=self.lse)
 
 
+def settle(parts, seconds, max_steps=20000):
+    """Run untimed steps back to back for `seconds` of wall time.
+
+    Coming out of idle, the GPU raises its clocks over the first tens of
+    milliseconds of sustained work: on one MI355X the Llama-3 prefill took
+    0.60 ms per call at first and 0.475 ms from about the 40th call on. A few
+    warmup steps end inside that ramp, so the timed steps would measure it
+    instead of the kernels. Steps go out in batches of 8 between
+    synchronisations, so the GPU stays busy. Returns the steps run."""
+    import torch
+    n = 0
+    t_end = time.perf_counter() + seconds
+    while n < max_steps and time.perf_counter() < t_end:
+        for _ in range(8):
+            for p in parts:
+                p()
+        n += 8
+        torch.cuda.synchronize()
+    return n
+
+
 def time_steps(parts, steps, warmup):
     """Warm up, then time exactly `steps` steps; per-part event timings."""
     import torch
@@ -528,6 +551,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed steps before the warmup steps (GPU clock ramp-up)")
     ap.add_argument("--config", default="default")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -581,6 +606,7 @@ def main():
         dec = DecodePaged(fa, num_splits=args.num_splits) if paged else Decode(fa, num_splits=args.num_splits)
         parts.append(dec)
 
+    n_settle = settle(parts, args.settle) if args.settle > 0 else 0
     wall, per = time_steps(parts, args.steps, args.warmup)
     ms_per_step = wall * 1e3 / args.steps
     out = {"metric": "attn fwd TFLOP/s & % MFMA peak, Llama-3-8B GQA causal N=8192; decode GB/s"}
@@ -621,7 +647,8 @@ def main():
         if pre is None:
             out.update(value=round(gbs, 1), unit="GB/s", roofline=droof)
     out.update({
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "settle": {"seconds": args.settle, "steps": n_settle}, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": ("fp8e4m3" if cfg.endswith("_fp8") else "bf16" if cfg not in ("mha_n4096_fp16", "mha_n4096_fp16_causal")
                   else "fp16"),
         "data": ("synthetic: seeded N(0,1) quantized to E4M3 per (batch, head) slab" if cfg.endswith("_fp8")
