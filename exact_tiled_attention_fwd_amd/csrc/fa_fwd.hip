@@ -138,8 +138,10 @@ struct DmaReader {
 // The 8 tile loads of one step, slotted in after every (N / 8)-th MFMA of an
 // N-op matrix-core phase (MFMAs 2, 6, ..., 30 of 32; 1, 3, ..., 15 of 16), so
 // that the loads of the four loading waves reach the address unit a few at a
-// time instead of in one burst. Full tiles only.
-template <int N>
+// time instead of in one burst. Full tiles only. With ALWAYS the loads are
+// issued unconditionally (no branch splits the phase): the caller points a
+// tile that does not exist at tile 0 and its ring slot, which no wave reads.
+template <int N, bool ALWAYS = false>
 struct DmaSpread {
   const uint16_t* kbase;
   const uint16_t* vbase;
@@ -153,9 +155,9 @@ struct DmaSpread {
     if (t % ST != ST / 2) return;
     const int j = t / ST;
     if (j < 4) {
-      if (has_k) dma16(kbase + kstep * j, dk, kslot + 4096 * j);
+      if (ALWAYS || has_k) dma16(kbase + kstep * j, dk, kslot + 4096 * j);
     } else {
-      if (has_v) dma16(vbase + vstep * (j - 4), dv, vslot + 4096 * (j - 4));
+      if (ALWAYS || has_v) dma16(vbase + vstep * (j - 4), dv, vslot + 4096 * (j - 4));
     }
   }
 };
@@ -168,7 +170,9 @@ struct DmaSpread {
 // math of Flash Attention" through LDS. Tiles, ring and loads are those of
 // the 256-row mode; the second block's Q and first K and V tiles are loaded
 // while the first is joined and written.
-template <int DT, int D, bool CAUSAL, bool VARLEN, bool SPLIT>
+// ALIGNED: every key tile is full (Nk a multiple of the tile rows), so the
+// loads of a full matrix-core phase need no branch.
+template <int DT, int D, bool CAUSAL, bool VARLEN, bool SPLIT, bool ALIGNED>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int Nq_all, int Nk_all,
@@ -352,8 +356,19 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_kernel(
       for (int i = 0; i <= n_kv; ++i) {
         const bool do_o = i >= 1 && i - 1 < wave_tiles, do_s = i < wave_tiles;
         const bool has_k = i + 2 < n_kv, has_v = i + 1 < n_kv;
-        const int n_new = 4 * has_k + 4 * has_v;
-        if (do_o && do_s) {
+        int n_new = 4 * has_k + 4 * has_v;
+        if (ALIGNED && do_o && do_s) {
+          // all 8 loads, a missing K_{i+2} / V_{i+1} re-reading tile 0 into
+          // the slot that tile would have had (read by no wave)
+          const DmaSpread<MmaPlan<D, WR, true, true, Rd>::N, true> ex{
+              has_k ? kp + (long long)(i + 2) * ROWS * sl.ks : kp, has_v ? vp + (long long)(i + 1) * ROWS * sl.vs : vp,
+              lds_k + (uint32_t)(((i + 2) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
+              lds_v + (uint32_t)(((i + 1) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
+              true, true, dk, dv, kstep, vstep};
+          mma_run<DT, D, WR, true, true, Rd>(obuf, vring + ((i - 1) % kSlots) * kTile + koff,
+                                             kring + (i % kSlots) * kTile + koff, pk, qop, acc_o, s, lane, ex);
+          n_new = 8;
+        } else if (do_o && do_s) {
           // full phase: with full tiles the loads are spread over its MFMAs
           const bool spread = (!has_k || Nk - (i + 2) * ROWS >= ROWS) && (!has_v || Nk - (i + 1) * ROWS >= ROWS);
           if (!spread) issue_step(i);
@@ -502,15 +517,25 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     if (use_split(nblocks, rows)) {
       const int n_pairs = ((rows + kBMs - 1) / kBMs + 1) / 2;
       const long long nsplit = (long long)n_pairs * a.B * a.Hq;
-      hipLaunchKernelGGL((fa_fwd_kernel<DT, D, true, false, true>), dim3((unsigned)nsplit), dim3(kThreads), 0,
-                         stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                         a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_pairs, vl, a.layout);
+      if (a.Nk % (8192 / D) == 0)
+        hipLaunchKernelGGL((fa_fwd_kernel<DT, D, true, false, true, true>), dim3((unsigned)nsplit), dim3(kThreads), 0,
+                           stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
+                           a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_pairs, vl, a.layout);
+      else
+        hipLaunchKernelGGL((fa_fwd_kernel<DT, D, true, false, true, false>), dim3((unsigned)nsplit), dim3(kThreads), 0,
+                           stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
+                           a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_pairs, vl, a.layout);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((fa_fwd_kernel<DT, D, CAUSAL, VARLEN, false>), dim3((unsigned)nblocks), dim3(kThreads), 0,
-                     stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_qt, vl, a.layout);
+  if (!VARLEN && a.Nk % (8192 / D) == 0)
+    hipLaunchKernelGGL((fa_fwd_kernel<DT, D, CAUSAL, VARLEN, false, !VARLEN>), dim3((unsigned)nblocks), dim3(kThreads),
+                       0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
+                       a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_qt, vl, a.layout);
+  else
+    hipLaunchKernelGGL((fa_fwd_kernel<DT, D, CAUSAL, VARLEN, false, false>), dim3((unsigned)nblocks), dim3(kThreads),
+                       0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
+                       a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, n_qt, vl, a.layout);
   return hipGetLastError();
 }
 
