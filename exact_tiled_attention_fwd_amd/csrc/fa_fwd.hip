@@ -96,6 +96,7 @@ __device__ __attribute__((always_inline)) inline void dma16(const uint16_t* sbas
 // 8, wave-uniform) direct-to-LDS loads outstanding. No release fence: it
 // would also wait for the loads that are meant to stay in flight.
 __device__ __attribute__((always_inline)) inline void dma_barrier(int pending) {
+  pending = __builtin_amdgcn_readfirstlane(pending);  // wave-uniform: scalar branches
   if (pending >= 8)
     __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
   else if (pending >= 4)
