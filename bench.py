@@ -622,15 +622,16 @@ def main():
                           "ms_median": round(float(np.median(per[i])), 4),
                           "ms_min": round(float(np.min(per[i])), 4), "tflops": round(tflops, 2),
                           "frac_mfma_peak": round(tflops / peak, 4)}
-        prof = cfg if cfg in ("llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd", "llama3_8b_gqa_n8192_fp8") else pname
+        prof = cfg if cfg in ("llama3_8b_gqa_varlen", "llama3_8b_gqa_n8192_bshd", "llama3_8b_gqa_n8192_fp8",
+                              "mha_n4096_fp16_causal") else pname
         kind = "bwd" if cfg.endswith("_bwd") else "fwd"
-        traffic = counter_traffic(f"fa_{kind}_{prof}_counters.md") if causal else None
+        traffic = counter_traffic(f"fa_{kind}_{prof}_counters.md")
         out["roofline"] = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                            "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": traffic,
                            "algorithmic_bytes": pre.bytes, "flops_per_launch": pre.flops}
         # The published peak assumes 2.4 GHz; the committed profile records the
         # clock the kernel actually ran at, and the fraction of the peak at it.
-        ghz = counter_clock_ghz(f"fa_{kind}_{prof}_counters.md") if causal else None
+        ghz = counter_clock_ghz(f"fa_{kind}_{prof}_counters.md")
         if ghz:
             out["roofline"]["clock_ghz"] = ghz
             out["roofline"]["frac_at_clock"] = round(tflops / (peak * ghz / 2.4), 4)
