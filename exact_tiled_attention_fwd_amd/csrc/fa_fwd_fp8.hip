@@ -99,6 +99,7 @@ __device__ __attribute__((always_inline)) inline void dma16(const uint8_t* sbase
 // Barrier after waiting until this thread has at most `pending` (0, 2 or 4,
 // wave-uniform) direct-to-LDS loads outstanding.
 __device__ __attribute__((always_inline)) inline void dma_barrier(int pending) {
+  pending = __builtin_amdgcn_readfirstlane(pending);  // wave-uniform: scalar branches
   if (pending >= 4)
     __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
   else if (pending >= 2)
@@ -199,7 +200,11 @@ __device__ __attribute__((always_inline)) inline void softmax8(const f32x16 (&s)
 
 // The 4 tile loads of one step (K_{i+2}: 2, V_{i+1}: 2 instructions per
 // wave), slotted in after MFMAs 1, 3, 5, 7 of a full 8-op matrix-core phase.
-// Full tiles only.
+// Full tiles only. With ALWAYS the loads carry no branch (which would split
+// the phase into several scheduling regions): the caller points a tile that
+// does not exist at tile 0 and at the ring slot it would have had, which no
+// wave reads.
+template <bool ALWAYS = false>
 struct DmaSpread {
   const uint8_t* kbase;
   const uint8_t* vbase;
@@ -210,9 +215,9 @@ struct DmaSpread {
     if ((t & 1) == 0) return;
     const int j = t >> 1;
     if (j < 2) {
-      if (has_k) dma16(kbase + 32 * kD * j, dk, kslot + 4096 * j);
+      if (ALWAYS || has_k) dma16(kbase + 32 * kD * j, dk, kslot + 4096 * j);
     } else {
-      if (has_v) dma16(vbase + 32 * kD * (j - 2), dv, vslot + 4096 * (j - 2));
+      if (ALWAYS || has_v) dma16(vbase + 32 * kD * (j - 2), dv, vslot + 4096 * (j - 2));
     }
   }
 };
@@ -220,7 +225,8 @@ struct NoDma {
   __device__ void operator()(int) const {}
 };
 
-template <bool CAUSAL>
+// ALIGNED: every key tile is full (Nk a multiple of the tile rows).
+template <bool CAUSAL, bool ALIGNED>
 __global__ __launch_bounds__(kThreads, 1) void fa_fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, const float* __restrict__ q_ds,
@@ -388,12 +394,21 @@ __global__ __launch_bounds__(kThreads, 1) void fa_fwd_fp8_kernel(
     for (int i = 0; i <= n_kv; ++i) {
       const bool do_o = i >= 1 && i - 1 < wt, do_s = i < wt;
       const bool has_k = i + 2 < n_kv, has_v = i + 1 < n_kv;
-      const int n_new = 2 * has_k + 2 * has_v;
-      if (do_o && do_s) {
+      int n_new = 2 * has_k + 2 * has_v;
+      if (ALIGNED && do_o && do_s) {
+        // all 4 loads; a missing K_{i+2} / V_{i+1} re-reads tile 0
+        const DmaSpread<true> ex{has_k ? kp + (size_t)(i + 2) * kRows * kD : kp,
+                                 has_v ? vp + (size_t)(i + 1) * kRows * kD : vp,
+                                 lds_k + (uint32_t)(((i + 2) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
+                                 lds_v + (uint32_t)(((i + 1) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
+                                 true, true, dk, dv};
+        mma_t(std::true_type{}, std::true_type{}, i - 1, i, ex);
+        n_new = 4;
+      } else if (do_o && do_s) {
         // full phase: with full tiles the loads are spread over its MFMAs
         const bool spread = (!has_k || Nk - (i + 2) * kRows >= kRows) && (!has_v || Nk - (i + 1) * kRows >= kRows);
         if (!spread) issue_step(i);
-        const DmaSpread ex{kp + (size_t)(i + 2) * kRows * kD, vp + (size_t)(i + 1) * kRows * kD,
+        const DmaSpread<> ex{kp + (size_t)(i + 2) * kRows * kD, vp + (size_t)(i + 1) * kRows * kD,
                            lds_k + (uint32_t)(((i + 2) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
                            lds_v + (uint32_t)(((i + 1) % kSlots) * kTile) + (uint32_t)(64 * wg * 16),
                            has_k && spread, has_v && spread, dk, dv};
@@ -436,9 +451,14 @@ hipError_t launch_t(const Fp8Args& a, hipStream_t stream) {
   const int n_qt = (a.Nq + kBM - 1) / kBM;
   const long long nblocks = (long long)n_qt * a.B * a.Hq;
   if (nblocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa_fwd_fp8_kernel<CAUSAL>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream, a.q, a.k, a.v,
-                     (uint16_t*)a.o, a.lse, a.q_descale, a.k_descale, a.v_descale, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
-                     a.scale * kLog2e, n_qt);
+  if (a.Nk % kRows == 0)
+    hipLaunchKernelGGL((fa_fwd_fp8_kernel<CAUSAL, true>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream, a.q, a.k,
+                       a.v, (uint16_t*)a.o, a.lse, a.q_descale, a.k_descale, a.v_descale, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
+                       a.scale * kLog2e, n_qt);
+  else
+    hipLaunchKernelGGL((fa_fwd_fp8_kernel<CAUSAL, false>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream, a.q, a.k,
+                       a.v, (uint16_t*)a.o, a.lse, a.q_descale, a.k_descale, a.v_descale, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
+                       a.scale * kLog2e, n_qt);
   return hipGetLastError();
 }
 
