@@ -57,6 +57,30 @@ def test_small_shapes(fa, case):
     full_case(fa, 100 + SMALL.index(case), *case)
 
 
+# Key counts that are whole tiles (64 keys at d = 128, 128 at d = 64) with
+# only a few tiles: the last two steps of every such launch issue their loads
+# without a branch, re-reading tile 0 into the slot of a tile that does not
+# exist, so these shapes are mostly such steps.
+ALIGNED = [
+    # B, Hq, Hkv, Nq, Nk, d, dtype, causal
+    (1, 4, 2, 64, 64, 128, ai.BF16, False),
+    (1, 4, 2, 128, 128, 128, ai.BF16, True),
+    (2, 4, 1, 192, 192, 128, ai.FP16, True),
+    (1, 8, 2, 100, 320, 128, ai.BF16, True),    # Nq < Nk, bottom-right causal
+    (1, 2, 2, 300, 192, 128, ai.BF16, False),   # Nq > Nk
+    (1, 4, 4, 128, 128, 64, ai.FP16, True),
+    (2, 4, 2, 256, 256, 64, ai.BF16, False),
+    (1, 8, 2, 384, 384, 64, ai.FP16, True),
+    (1, 4, 1, 50, 512, 64, ai.BF16, True),
+]
+
+
+@pytest.mark.parametrize("case", ALIGNED,
+                         ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}Nq{c[3]}Nk{c[4]}d{c[5]}{c[6]}{'c' if c[7] else 'n'}" for c in ALIGNED])
+def test_aligned_few_tiles(fa, case):
+    full_case(fa, 200 + ALIGNED.index(case), *case)
+
+
 def sampled_case(fa, name, causal, rows_per_head):
     c = ai.CONFIGS[name]
     B, Hq, Hkv, N, d, dt = c["B"], c["Hq"], c["Hkv"], c["N"], c["d"], c["dtype"]
